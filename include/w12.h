@@ -1,0 +1,190 @@
+/*
+ * w12.h -- C ABI of libw12: lossless 12-bit (W12) weight streaming for the
+ * verification pass of greedy speculative decoding, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources for what each call computes:
+ *   [S1] "SpecPilot: Autonomous Algorithm Discovery and Systems Optimization
+ *        for Speculative Decoding", long-form summary (jaehun.me):
+ *        section 1.1 (greedy acceptance), 1.2 (lossless = exact-pass argmax),
+ *        4.1 (W12 format, 12 KB records, deterministic stream-K GEMM, LM
+ *        head argmax), 4.3 (tree verification: longest matching path + bonus).
+ *   [S2] the same paper's digest page (agihunt.info), W12 paragraph (sign +
+ *        4-bit exponent offset + all 7 mantissa bits, load-time check).
+ *   [S3] "Speculative decoding" (poot-llm docs), "What a round guarantees"
+ *        (greedy rows keep drafts equal to the argmax, then one more token)
+ *        and "What is refused" (typed refusal before anything runs).
+ *
+ * Conventions (all calls):
+ *   - Every pointer argument is DEVICE memory owned by the caller, except
+ *     `const w12_matrix *` descriptors and `size_t *` / `int64_t` outputs of
+ *     the *_workspace queries, which live in host memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return as soon as the kernels are enqueued.
+ *   - Argument errors return W12_EINVAL before anything is launched (null
+ *     pointers, shapes the format cannot hold, m outside [1, 256], bf16
+ *     matrices / records / x / y not 16-byte aligned, u32 arrays not 4-byte
+ *     aligned); a
+ *     workspace smaller than its query returns W12_ENOSPC; a failed launch
+ *     returns W12_EHIP.  Errors found on the device (a corrupt packed
+ *     weight, an invalid tree) are reported through outputs, as each call
+ *     states.  The library never allocates memory.
+ *   - Workspaces ("ws") must be zero-filled before their first use. A
+ *     workspace holds arrival counters, which every completed call returns
+ *     to zero, and partial sums, which a call writes before it reads them;
+ *     so one allocation serves any number of calls.  Calls that overlap in
+ *     time must not share a workspace.
+ *
+ * W12 layout (readings of [S1] 4.1 and [S2] for gfx950):
+ *   N output channels x K inputs, N % 32 == 0, K % 256 == 0, K <= 2^20.
+ *   e_top[n]   window top E_n (biased bf16 exponent) in [16, 254]; the
+ *              window [E_n - 15, E_n] is the one holding the most normal
+ *              weights of channel n (smallest E_n on ties).
+ *   records    N*K*3/2 bytes; record (s, r) = channels [32s, 32s+32) x
+ *              k [256r, 256r+256) at byte (s*(K/256) + r) * 12288.  Bytes
+ *              [0, 8192) hold the 8-bit view hi8 = s<<7 | o<<3 | m>>4
+ *              (o = e - (E_n - 15)), bytes [8192, 12288) the low mantissa
+ *              nibbles.  Weight (c, k') of a record, subtile t = k'/32,
+ *              half h = (k'%32)/16, j = k'%16, lane = c + 32h:
+ *                hi8 at t*1024 + lane*16 + j,
+ *                lo4 at 8192 + t*512 + lane*8 + 4*(j/8) + j%4, high nibble
+ *                when j%8 < 4, low nibble otherwise.
+ *              Escaped weights (zero, denormal, Inf/NaN, out of window) hold
+ *              code 0 and are listed in `esc`.
+ *   esc_off    [N*K/1024 + 1] u32 offsets into esc, one per escape block
+ *              (strip s, record r, subtile t), block id (s*(K/256)+r)*8 + t.
+ *   esc        [esc_off[last]] u32 entries bits<<16 | c<<5 | kk, c the
+ *              channel in the strip, kk = k % 32; (c, kk) ascending within a
+ *              block, so each channel's list runs in ascending k.
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W12_OK = 0,
+  W12_EINVAL = -1, /* bad argument; nothing launched                     */
+  W12_ENOSPC = -2, /* workspace smaller than the matching query          */
+  W12_EHIP = -3    /* a HIP runtime call or kernel launch failed         */
+} w12_status;
+
+typedef enum { W12_Y_F32 = 0, W12_Y_BF16 = 1 } w12_ydtype;
+
+/* Device-resident W12 matrix (the five buffers above). */
+typedef struct w12_matrix {
+  int64_t n, k;
+  const uint8_t *records;
+  const uint8_t *e_top;
+  const uint32_t *esc_off;
+  const uint32_t *esc;
+} w12_matrix;
+
+/* Human-readable name of a w12_status (static string). */
+const char *w12_strerror(int status);
+
+/* ABI version, bumped on any layout or signature change. */
+int w12_abi_version(void);
+
+/* Number of escape blocks N*K/1024; esc_off holds one more entry. */
+int64_t w12_num_blocks(int64_t n, int64_t k);
+
+/*
+ * w12_pack_plan -- first half of packing ([S1] 4.1: conversion at load).
+ *   w        [n, k] bf16 bit patterns, row-major (read only).
+ *   e_top    [n] out: window tops E_n.
+ *   esc_off  [w12_num_blocks(n,k) + 1] out: escape offsets; esc_off[last]
+ *            is the escape count the caller reads to size `esc`.
+ */
+w12_status w12_pack_plan(const uint16_t *w, int64_t n, int64_t k,
+                         uint8_t *e_top, uint32_t *esc_off, hipStream_t stream);
+
+/*
+ * w12_pack -- second half: writes the records and the escape entries.
+ *   e_top, esc_off  from w12_pack_plan on the same w.
+ *   records         [n*k*3/2] out.
+ *   esc             [esc_capacity] out; entries past esc_capacity are
+ *                   dropped (the load-time check then fails), so pass
+ *                   esc_capacity >= esc_off[last].
+ */
+w12_status w12_pack(const uint16_t *w, int64_t n, int64_t k,
+                    const uint8_t *e_top, const uint32_t *esc_off,
+                    uint8_t *records, uint32_t *esc, int64_t esc_capacity,
+                    hipStream_t stream);
+
+/* w12_decode -- restore the bf16 weights [n, k] (row-major) exactly
+ * ([S1] 4.1: escapes restored exactly; the same in-register decode the GEMM
+ * uses). */
+w12_status w12_decode(const w12_matrix *w, uint16_t *out, hipStream_t stream);
+
+/* w12_check -- load-time bit-for-bit check ([S1] 4.1, [S2]): decodes every
+ * weight and ADDS the number that differ from ref [n, k] to *mismatches
+ * (device u64; the caller zeroes it). Non-zero means refuse the weights. */
+w12_status w12_check(const w12_matrix *w, const uint16_t *ref,
+                     unsigned long long *mismatches, hipStream_t stream);
+
+/* Workspace bytes w12_gemm needs for this shape (host output). */
+w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
+
+/*
+ * w12_gemm -- verify GEMM ([S1] 4.1): y[i, c] = sum_k x[i, k] * W[c, k] for
+ * the m verify rows, streaming every W12 record from HBM once, restoring it
+ * in registers, fp32 accumulation. Rows m < 16 use a VALU dot-product path,
+ * m >= 16 bf16 MFMA. The reduction over k is split across workgroups in a
+ * fixed order (stream-K), so results are bitwise reproducible.
+ *   x   [m, k] bf16 row-major, 1 <= m <= 256.
+ *   y   [m, n] row-major, fp32 (W12_Y_F32) or bf16 (W12_Y_BF16, the
+ *       round-to-nearest-even of the same fp32 result).
+ *   ws  zero-filled workspace of >= w12_gemm_workspace bytes.
+ */
+w12_status w12_gemm(const w12_matrix *w, const uint16_t *x, int64_t m,
+                    void *y, int ytype, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes w12_head_argmax needs (host output). */
+w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
+
+/*
+ * w12_head_argmax -- LM head + greedy token ([S1] 1.1, 4.1): for each verify
+ * row i, idx[i] = the lowest vocabulary id v attaining max_v logits[i, v],
+ * logits = x W^T computed as in w12_gemm (never written to memory).
+ *   idx     [m] int32 out; maxval [m] fp32 out (may be NULL).
+ */
+w12_status w12_head_argmax(const w12_matrix *head, const uint16_t *x, int64_t m,
+                           int32_t *idx, float *maxval, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * tree_accept -- greedy tree verification ([S1] 1.1, 4.3; [S3]).
+ * Trees are concatenated: tree t owns nodes [node_off[t], node_off[t+1]),
+ * node_off[0] = 0, node_off[num_trees] = total_nodes; node i of a tree is
+ * verify row node_off[t] + i, with tree-local parent[i] (-1 for the root,
+ * else in [0, i)), draft token token[i] and the target's argmax[i] for that
+ * row. A node is accepted when every edge on its root path satisfies
+ * token[child] == argmax[parent]. Per tree:
+ *   accept_len[t] = depth of the deepest accepted node (lowest index on
+ *                   ties) = number of accepted drafts (tau = accept_len+1);
+ *   path[node_off[t] + j] = tree-local node at depth j of that path for
+ *                   j <= accept_len, -1 after it;
+ *   bonus[t]      = argmax of the deepest accepted node's row.
+ * A tree with no nodes, a root parent other than -1, a parent outside
+ * [0, i), or offsets outside [0, total_nodes] gets accept_len = bonus = -1
+ * and an all -1 path (device-detected; the call itself returns W12_OK).
+ */
+w12_status tree_accept(int32_t num_trees, const int32_t *node_off,
+                       int32_t total_nodes, const int32_t *parent,
+                       const int32_t *token, const int32_t *argmax,
+                       int32_t *accept_len, int32_t *path, int32_t *bonus,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W12_H */

@@ -1,0 +1,403 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars: packing, decode, argmax indices (away from near-ties) and accepted
+paths bit-exact; GEMM outputs within |y - y_ref| <= 2e-3 sum|x w| + 1e-6.
+Sizes span several records/tiles, odd strip counts and ragged stream-K
+slices; the full-size shapes are checked on sampled outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import verify as V
+from oracle import w12_format as F
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="session")
+def w12():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import w12_weight_streaming_amd as w
+    w.lib()
+    return w
+
+
+DEV = "cuda:0"
+
+
+def gen(n, k, seed, **kw):
+    return synth.weights_bf16(n, k, seed, **kw)
+
+
+def special_matrix(n=64, k=512, seed=9):
+    """Zeros, -0, denormals, Inf/NaN payloads, window edges, empty channels."""
+    rng = np.random.default_rng(seed)
+    s = rng.integers(0, 2, (n, k), dtype=np.uint32)
+    e = rng.integers(100, 125, (n, k), dtype=np.uint32)
+    m = rng.integers(0, 128, (n, k), dtype=np.uint32)
+    w = ((s << 15) | (e << 7) | m).astype(np.uint16)
+    w[rng.random((n, k)) < 0.05] = 0
+    w[rng.random((n, k)) < 0.02] = 0x8000
+    w[rng.random((n, k)) < 0.02] = 0x0013
+    w[rng.random((n, k)) < 0.01] = 0x7F80
+    w[rng.random((n, k)) < 0.01] = 0xFFC3
+    w[3, :] = 0                        # all-zero channel
+    w[4, :] = 0x0080                   # exponent 1 only
+    w[5, :] = 0x7F7F                   # exponent 254 only
+    w[6, ::2] = (140 << 7) | 5         # two clusters 40 binades apart
+    w[6, 1::2] = (100 << 7) | 3
+    w[7, :300] = 0x0001                # a block with > 64 escapes
+    return w
+
+
+def pack_gpu(w12, bits):
+    t = synth.from_bits(bits, DEV)
+    return w12.w12_pack(t), t
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_pack_equal(pw, ref):
+    assert np.array_equal(host(pw.records), ref["records"])
+    assert np.array_equal(host(pw.e_top), ref["e_top"])
+    assert np.array_equal(host(pw.esc_off).view(np.uint32), ref["esc_off"])
+    assert pw.n_esc == len(ref["esc"])
+    assert np.array_equal(host(pw.esc)[:pw.n_esc].view(np.uint32), ref["esc"])
+
+
+# ----------------------------------------------------------------------------- pack / decode
+
+@pytest.mark.parametrize("shape,kw", [
+    ((1024, 1024), dict(p_zero=0.01, p_outlier=0.001)),          # config-1 parity case
+    ((32, 256), dict(p_zero=0.01, p_outlier=0.001)),
+    ((96, 768), dict(p_zero=0.03, p_outlier=0.02)),              # odd strip count
+    ((160, 1280), dict(p_zero=0.0, p_outlier=0.0)),
+])
+def test_pack_bitexact(w12, shape, kw):
+    n, k = shape
+    say("pack", shape, kw)
+    bits = synth.bits_u16(gen(n, k, 101 + n, **kw))
+    pw, t = pack_gpu(w12, bits)
+    assert_pack_equal(pw, F.pack(bits))
+    assert w12.w12_check(pw, t) == 0
+    assert np.array_equal(synth.bits_u16(w12.w12_decode(pw)), bits)
+
+
+def test_pack_special_values(w12):
+    bits = special_matrix()
+    pw, t = pack_gpu(w12, bits)
+    assert_pack_equal(pw, F.pack(bits))
+    assert np.array_equal(synth.bits_u16(w12.w12_decode(pw)), bits)
+    assert w12.w12_check(pw, t) == 0
+
+
+def upload_packed(w12, ref, n, k):
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(DEV)
+    esc = ref["esc"] if len(ref["esc"]) else np.zeros(1, np.uint32)
+    return w12.PackedW12(n, k, d(ref["records"], np.uint8), d(ref["e_top"], np.uint8),
+                         d(ref["esc_off"], np.int32), d(esc, np.int32), len(ref["esc"]))
+
+
+def test_decode_of_oracle_packed_buffers(w12):
+    for (n, k, seed) in ((64, 512, 3), (1024, 1024, 4)):
+        bits = synth.bits_u16(gen(n, k, seed, p_zero=0.02, p_outlier=0.01))
+        pw = upload_packed(w12, F.pack(bits), n, k)
+        assert np.array_equal(synth.bits_u16(w12.w12_decode(pw)), bits)
+    bits = special_matrix()
+    pw = upload_packed(w12, F.pack(bits), 64, 512)
+    assert np.array_equal(synth.bits_u16(w12.w12_decode(pw)), bits)
+
+
+def test_check_detects_corruption(w12):
+    bits = synth.bits_u16(gen(64, 512, 5))
+    pw, t = pack_gpu(w12, bits)
+    rec = pw.records.clone()
+    pw.records[777] ^= 0x10
+    assert w12.w12_check(pw, t) >= 1
+    pw.records.copy_(rec)
+    pw.e_top[3] += 1
+    assert w12.w12_check(pw, t) >= 1
+    pw.e_top[3] -= 1
+    assert w12.w12_check(pw, t) == 0
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+GEMM_SHAPES = [(1024, 1024), (96, 768), (320, 1792)]
+ROWS = [1, 2, 3, 5, 8, 15, 16, 17, 32, 33, 64, 100, 192, 256]
+
+
+@pytest.fixture(scope="module")
+def gemm_mats(w12):
+    mats = {}
+    for (n, k) in GEMM_SHAPES:
+        bits = synth.bits_u16(gen(n, k, 7 * n + k, p_zero=0.03, p_outlier=0.02))
+        pw, _ = pack_gpu(w12, bits)
+        mats[(n, k)] = (pw, bits)
+    return mats
+
+
+@pytest.mark.parametrize("m", ROWS)
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm_within_tolerance(w12, gemm_mats, shape, m):
+    pw, bits = gemm_mats[shape]
+    say("gemm", shape, "m", m)
+    x = synth.activations_bf16(m, shape[1], 11 + m)
+    y = w12.w12_gemm(pw, x.to(DEV))
+    y_ref, bound = V.gemm_ref(synth.bits_u16(x), bits)
+    ok = V.within_tolerance(host(y), y_ref, bound)
+    assert ok.all(), f"{(~ok).sum()} outputs out of tolerance"
+    yb = w12.w12_gemm(pw, x.to(DEV), out_dtype=torch.bfloat16)
+    assert torch.equal(yb.cpu(), y.cpu().to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_gemm_exact_pins(w12, m):
+    """One-hot rows give weight columns exactly; small integers are exact."""
+    n, k = 320, 1024
+    bits = synth.bits_u16(gen(n, k, 21, p_zero=0.05, p_outlier=0.02))
+    pw, _ = pack_gpu(w12, bits)
+    x = np.zeros((m, k), np.uint16)
+    cols = np.random.default_rng(m).choice(k, m, replace=False)
+    x[np.arange(m), cols] = 0x3F80
+    y = host(w12.w12_gemm(pw, synth.from_bits(x, DEV)))
+    wf = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(y, wf[:, cols].T)
+    rng = np.random.default_rng(m + 1)
+    xi = rng.integers(-8, 9, (m, k)).astype(np.float32)
+    wi = rng.integers(-8, 9, (n, k)).astype(np.float32)
+    wi[rng.random((n, k)) < 0.05] = 0.0          # zeros travel as escapes
+    wb = (wi.view(np.uint32) >> 16).astype(np.uint16)
+    xb = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    pw2, _ = pack_gpu(w12, wb)
+    y2 = host(w12.w12_gemm(pw2, synth.from_bits(xb, DEV)))
+    assert np.array_equal(y2, xi @ wi.T)
+
+
+@pytest.mark.parametrize("m", [1, 32])
+def test_gemm_deterministic_and_workspace_reuse(w12, m):
+    """Bitwise repeatable (fixed-order stream-K), and a reused workspace gives
+    the same bits as a fresh zero-filled one (its counters return to zero)."""
+    n, k = 5120, 6144
+    w = gen(n, k, 31, device=DEV)
+    pw = w12.w12_pack(w)
+    x = synth.activations_bf16(m, k, 32, device=DEV)
+    y1 = w12.w12_gemm(pw, x).clone()
+    for _ in range(3):
+        y2 = w12.w12_gemm(pw, x).clone()
+        assert torch.equal(y1, y2)
+    fresh = torch.zeros(w12.gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=DEV)
+    assert torch.equal(y1, w12.w12_gemm(pw, x, ws=fresh))
+    idx1, mx1 = w12.w12_head_argmax(pw, x)
+    idx1, mx1 = idx1.clone(), mx1.clone()
+    for _ in range(3):
+        idx2, mx2 = w12.w12_head_argmax(pw, x)
+        assert torch.equal(idx1, idx2) and torch.equal(mx1, mx2)
+    assert torch.equal(mx1, y1[torch.arange(m, device=DEV), idx1.long()])
+
+
+def test_workspace_shared_across_shapes(w12):
+    """One workspace, calls of different shapes interleaved (the partial sums
+    of one shape must never sit where another keeps its counters)."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    shapes = [(64, 512), (2048, 1024), (96, 768), (4096, 512)]
+    mats = []
+    for i, (n, k) in enumerate(shapes):
+        bits = synth.bits_u16(gen(n, k, 300 + i, p_zero=0.02, p_outlier=0.01))
+        mats.append((w12.w12_pack(synth.from_bits(bits, DEV)), bits))
+    for rep in range(2):
+        for (pw, bits), m in zip(mats * 2, (1, 33, 7, 64, 16, 2, 48, 1)):
+            x = synth.activations_bf16(m, pw.k, 400 + m)
+            y = host(w12.w12_gemm(pw, x.to(DEV), ws=ws))
+            y_ref, bound = V.gemm_ref(synth.bits_u16(x), bits)
+            assert V.within_tolerance(y, y_ref, bound).all(), (pw.n, pw.k, m)
+
+
+def test_gemm_rejects_small_workspace(w12):
+    n, k = 256, 512
+    pw = w12.w12_pack(gen(n, k, 1, device=DEV))
+    x = synth.activations_bf16(32, k, 2, device=DEV)
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(w12.W12Error) as e:
+        w12.w12_gemm(pw, x, ws=small)
+    assert e.value.status == w12.W12_ENOSPC
+
+
+# ----------------------------------------------------------------------------- head argmax
+
+def check_argmax(idx, ref_idx, cands):
+    near = 0
+    for r in range(len(ref_idx)):
+        if len(cands[r]) == 1:
+            assert idx[r] == ref_idx[r], f"row {r}: {idx[r]} != {ref_idx[r]}"
+        else:
+            near += 1
+            assert idx[r] in set(cands[r].tolist()), f"row {r}: {idx[r]} not in near-tie set"
+    return near
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 32, 48])
+def test_head_argmax(w12, m):
+    n, k = 8192, 1024
+    bits = synth.bits_u16(gen(n, k, 41, p_zero=0.01, p_outlier=0.001))
+    pw, _ = pack_gpu(w12, bits)
+    x = synth.activations_bf16(m, k, 42 + m)
+    idx, mx = w12.w12_head_argmax(pw, x.to(DEV))
+    ref_idx, ref_max, cands = V.head_argmax(synth.bits_u16(x), bits)
+    near = check_argmax(host(idx), ref_idx, cands)
+    say("head m", m, "near-ties", near)
+    y = host(w12.w12_gemm(pw, x.to(DEV)))
+    assert np.array_equal(host(mx), y[np.arange(m), host(idx)])
+
+
+def test_head_argmax_exact_ties(w12):
+    """Integer data: duplicated winning rows tie exactly; lowest id wins."""
+    n, k, m = 4096, 512, 32
+    rng = np.random.default_rng(5)
+    xi = rng.integers(-2, 3, (m, k)).astype(np.float32)
+    wi = rng.integers(-2, 3, (n, k)).astype(np.float32)
+    for r in range(m):
+        win = 2 * np.sign(xi[r])
+        a, b = rng.choice(n, 2, replace=False)
+        wi[a] = win
+        wi[b] = win
+    xb = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    wb = (wi.view(np.uint32) >> 16).astype(np.uint16)
+    pw, _ = pack_gpu(w12, wb)
+    idx, _ = w12.w12_head_argmax(pw, synth.from_bits(xb, DEV))
+    L = xi.astype(np.int64) @ wi.astype(np.int64).T
+    expect = np.array([np.nonzero(L[r] == L[r].max())[0][0] for r in range(m)])
+    assert np.array_equal(host(idx), expect)
+
+
+# ----------------------------------------------------------------------------- tree acceptance
+
+def run_tree(w12, node_off, parent, token, argmax):
+    t = lambda a: torch.tensor(np.asarray(a, np.int32), device=DEV)
+    acc, path, bonus = w12.tree_accept(t(node_off), t(parent), t(token), t(argmax))
+    return host(acc), host(path), host(bonus)
+
+
+def test_tree_accept_random_forests(w12):
+    rng = np.random.default_rng(0)
+    for trees, nodes in ((1, 32), (24, 8), (7, 100), (3, 300)):
+        node_off, parent, token, argmax = [0], [], [], []
+        for ti in range(trees):
+            am = rng.integers(0, 50, nodes)
+            p, tk = synth.random_tree(nodes, 16, am, None, 0.7, seed=int(rng.integers(1 << 30)), vocab=50)
+            parent += list(p)
+            token += list(tk)
+            argmax += list(am)
+            node_off.append(node_off[-1] + nodes)
+        got = run_tree(w12, node_off, parent, token, argmax)
+        ref = V.tree_accept(node_off, parent, token, argmax)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r)
+
+
+def test_tree_accept_exhaustive_and_invalid(w12):
+    import itertools
+    node_off, parent, token, argmax = [0], [], [], []
+    rng = np.random.default_rng(1)
+    for n in range(1, 6):
+        for par in itertools.product(*[range(i) for i in range(1, n)]):
+            par = [-1] + list(par)
+            for mask in range(1 << (n - 1)):
+                am = list(rng.integers(0, 3, n))
+                tk = [0] + [am[par[i]] if (mask >> (i - 1)) & 1 else (am[par[i]] + 1) % 3
+                            for i in range(1, n)]
+                parent += par
+                token += tk
+                argmax += am
+                node_off.append(node_off[-1] + n)
+    # invalid: root parent 0, self parent, forward parent, empty tree
+    for bad in ([0, 0], [-1, 1], [-1, 2, 0]):
+        parent += bad
+        token += [0] * len(bad)
+        argmax += [0] * len(bad)
+        node_off.append(node_off[-1] + len(bad))
+    node_off.append(node_off[-1])
+    got = run_tree(w12, node_off, parent, token, argmax)
+    ref = V.tree_accept(node_off, parent, token, argmax)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+    assert (got[0][-4:] == -1).all()
+
+
+def test_tree_accept_spec_example(w12):
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "spec_example_tree.json")) as f:
+        g = json.load(f)
+    for case in ("chain", "tree"):
+        c = g[case]
+        n = len(c["parent"])
+        acc, path, bonus = run_tree(w12, [0, n], c["parent"], c["token"], c["argmax"])
+        assert acc[0] == c["accept_len"] and bonus[0] == c["bonus"] and list(path) == c["path"]
+
+
+# ----------------------------------------------------------------------------- full-size shapes
+
+BLOCK = [("Wq", 6144, 5120), ("Wk", 1024, 5120), ("Wo", 5120, 6144),
+         ("Wup", 17408, 5120), ("Wdown", 5120, 17408)]
+
+
+@pytest.mark.parametrize("name,n,k", BLOCK)
+def test_full_size_block_matrices(w12, name, n, k):
+    say("full", name, n, k)
+    w = gen(n, k, 1000 + n + k, device=DEV)
+    pw = w12.w12_pack(w)                      # includes the full bit-exact check
+    rng = np.random.default_rng(n)
+    for s in rng.choice(n // 32, 2, replace=False):
+        bits = synth.bits_u16(w[32 * s:32 * s + 32])
+        ref = F.pack(bits)
+        rec = host(pw.records).reshape(n // 32, -1)[s]
+        assert np.array_equal(rec, ref["records"])
+        assert np.array_equal(host(pw.e_top)[32 * s:32 * s + 32], ref["e_top"])
+        nb = k // 256 * 8
+        off = host(pw.esc_off).view(np.uint32)[s * nb:(s + 1) * nb + 1].astype(np.int64)
+        assert np.array_equal(off - off[0], ref["esc_off"].astype(np.int64))
+        assert np.array_equal(host(pw.esc)[off[0]:off[-1]].view(np.uint32), ref["esc"])
+    for m in (1, 16, 32, 64):
+        x = synth.activations_bf16(m, k, 7 + m, device=DEV)
+        y = host(w12.w12_gemm(pw, x))
+        cols = rng.choice(n, 64, replace=False)
+        xb = synth.bits_u16(x)
+        wb = synth.bits_u16(w[torch.as_tensor(cols, device=DEV)])
+        y_ref, bound = V.gemm_ref(xb, wb)
+        assert V.within_tolerance(y[:, cols], y_ref, bound).all(), (name, m)
+
+
+def test_full_size_batched_m192(w12):
+    n, k = 5120, 17408
+    w = gen(n, k, 77, p_zero=0.03, p_outlier=0.02, device=DEV)
+    pw = w12.w12_pack(w)
+    x = synth.activations_bf16(192, k, 78, device=DEV)
+    y = host(w12.w12_gemm(pw, x))
+    rng = np.random.default_rng(3)
+    cols = rng.choice(n, 48, replace=False)
+    y_ref, bound = V.gemm_ref(synth.bits_u16(x), synth.bits_u16(w[torch.as_tensor(cols, device=DEV)]))
+    assert V.within_tolerance(y[:, cols], y_ref, bound).all()
+
+
+def test_full_size_head_argmax(w12):
+    n, k, m = 152064, 5120, 32
+    w = gen(n, k, 4242, device=DEV)
+    pw = w12.w12_pack(w)
+    x = synth.activations_bf16(m, k, 4243, device=DEV)
+    idx, _ = w12.w12_head_argmax(pw, x)
+    rows = [0, 7, 31]
+    wb = synth.bits_u16(w)
+    del w
+    ref_idx, _, cands = V.head_argmax(synth.bits_u16(x)[rows], wb, chunk=16384)
+    check_argmax(host(idx)[rows], ref_idx, cands)

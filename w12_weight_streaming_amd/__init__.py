@@ -1,0 +1,259 @@
+"""w12_weight_streaming_amd -- lossless 12-bit weight streaming for the
+verification pass of greedy speculative decoding on MI355X (gfx950).
+
+Thin ctypes binding over libw12.so (C ABI in include/w12.h), with the same
+names as the C entry points: w12_pack, w12_decode, w12_check, w12_gemm,
+w12_head_argmax, tree_accept. Every step of the path runs in the library's
+HIP kernels; this module only checks tensor dtypes/devices, passes device
+pointers and the current HIP stream, and keeps zero-filled workspaces.
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw12.so")
+
+W12_OK, W12_EINVAL, W12_ENOSPC, W12_EHIP = 0, -1, -2, -3
+W12_Y_F32, W12_Y_BF16 = 0, 1
+MFMA_MIN_ROWS = 16
+MAX_ROWS = 256
+
+_lib = None
+
+
+class W12Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().w12_strerror(status).decode()}")
+
+
+class W12Matrix(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("records", ctypes.c_void_p), ("e_top", ctypes.c_void_p),
+                ("esc_off", ctypes.c_void_p), ("esc", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libw12.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m w12_weight_streaming_amd.build`"
+                " (hipcc, gfx950). There is no fallback path.")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        mp = ctypes.POINTER(W12Matrix)
+        sig = {
+            "w12_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "w12_abi_version": (ctypes.c_int, []),
+            "w12_num_blocks": (i64, [i64, i64]),
+            "w12_pack_plan": (ctypes.c_int, [vp, i64, i64, vp, vp, vp]),
+            "w12_pack": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, i64, vp]),
+            "w12_decode": (ctypes.c_int, [mp, vp, vp]),
+            "w12_check": (ctypes.c_int, [mp, vp, vp, vp]),
+            "w12_gemm_workspace": (ctypes.c_int, [i64, i64, i64, ctypes.POINTER(sz)]),
+            "w12_gemm": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
+            "w12_head_argmax_workspace": (ctypes.c_int, [i64, i64, i64, ctypes.POINTER(sz)]),
+            "w12_head_argmax": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
+            "tree_accept": (ctypes.c_int, [i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return ["w12_strerror", "w12_abi_version", "w12_num_blocks", "w12_pack_plan", "w12_pack",
+            "w12_decode", "w12_check", "w12_gemm_workspace", "w12_gemm",
+            "w12_head_argmax_workspace", "w12_head_argmax", "tree_accept"]
+
+
+def _ok(status: int, what: str):
+    if status != W12_OK:
+        raise W12Error(status, what)
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+
+
+@dataclass
+class PackedW12:
+    """Device-resident W12 matrix: the five buffers of include/w12.h."""
+    n: int
+    k: int
+    records: torch.Tensor   # uint8 [n*k*3/2]
+    e_top: torch.Tensor     # uint8 [n]
+    esc_off: torch.Tensor   # int32 view of u32 [n*k/1024 + 1]
+    esc: torch.Tensor       # int32 view of u32 [n_esc] (at least 1 element)
+    n_esc: int
+
+    def desc(self) -> W12Matrix:
+        return W12Matrix(self.n, self.k, self.records.data_ptr(), self.e_top.data_ptr(),
+                         self.esc_off.data_ptr(), self.esc.data_ptr())
+
+    @property
+    def device(self):
+        return self.records.device
+
+    def nbytes(self) -> int:
+        """Packed bytes: records + e_top + esc_off + escape entries."""
+        return (self.records.numel() + self.e_top.numel() + 4 * self.esc_off.numel()
+                + 4 * self.n_esc)
+
+
+# ------------------------------------------------------------------ workspaces
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device: torch.device, tag: str = "gemm") -> torch.Tensor:
+    """Zero-filled device workspace, grown on demand and kept per (device,
+    stream, tag). The library leaves it zero-filled after every call."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream, tag)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------------ entry points
+
+def w12_pack(w: torch.Tensor, check: bool = True) -> PackedW12:
+    """Pack bf16 weights [n, k] (on the GPU) into W12; with check=True run the
+    load-time bit-for-bit check and raise if any weight fails to restore."""
+    _need(w, torch.bfloat16, "w", 2)
+    n, k = w.shape
+    dev = w.device
+    s = _stream(dev)
+    L = lib()
+    nb = L.w12_num_blocks(n, k)
+    if nb < 0:
+        raise W12Error(W12_EINVAL, f"w12_pack: shape {n}x{k}")
+    e_top = torch.empty(n, dtype=torch.uint8, device=dev)
+    esc_off = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    _ok(L.w12_pack_plan(_ptr(w), n, k, _ptr(e_top), _ptr(esc_off), s), "w12_pack_plan")
+    n_esc = int(esc_off[-1].item()) & 0xFFFFFFFF
+    records = torch.empty(n * k * 3 // 2, dtype=torch.uint8, device=dev)
+    esc = torch.empty(max(n_esc, 1), dtype=torch.int32, device=dev)
+    _ok(L.w12_pack(_ptr(w), n, k, _ptr(e_top), _ptr(esc_off), _ptr(records), _ptr(esc),
+                   n_esc, s), "w12_pack")
+    pw = PackedW12(n, k, records, e_top, esc_off, esc, n_esc)
+    if check:
+        bad = w12_check(pw, w)
+        if bad:
+            raise RuntimeError(f"W12 load-time check failed: {bad} weights differ")
+    return pw
+
+
+def w12_decode(pw: PackedW12) -> torch.Tensor:
+    out = torch.empty(pw.n, pw.k, dtype=torch.bfloat16, device=pw.device)
+    d = pw.desc()
+    _ok(lib().w12_decode(ctypes.byref(d), _ptr(out), _stream(pw.device)), "w12_decode")
+    return out
+
+
+def w12_check(pw: PackedW12, ref: torch.Tensor) -> int:
+    """Number of weights whose restore differs from ref (0 = bit-exact)."""
+    _need(ref, torch.bfloat16, "ref", 2)
+    if tuple(ref.shape) != (pw.n, pw.k):
+        raise ValueError("ref shape does not match the packed matrix")
+    cnt = torch.zeros(1, dtype=torch.int64, device=pw.device)
+    d = pw.desc()
+    _ok(lib().w12_check(ctypes.byref(d), _ptr(ref), _ptr(cnt), _stream(pw.device)), "w12_check")
+    return int(cnt.item())
+
+
+def gemm_workspace_bytes(n: int, k: int, m: int) -> int:
+    out = ctypes.c_size_t(0)
+    _ok(lib().w12_gemm_workspace(n, k, m, ctypes.byref(out)), "w12_gemm_workspace")
+    return out.value
+
+
+def w12_gemm(pw: PackedW12, x: torch.Tensor, out: torch.Tensor | None = None,
+             out_dtype=torch.float32, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m, n] = x[m, :] . W[n, :] with W streamed from W12 (fp32 accumulate)."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if k != pw.k:
+        raise ValueError(f"x has k={k}, matrix has k={pw.k}")
+    if out is None:
+        out = torch.empty(m, pw.n, dtype=out_dtype, device=x.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, pw.n):
+        raise ValueError("out must be [m, n] float32 or bfloat16")
+    _need(out, out.dtype, "out", 2)
+    yt = W12_Y_F32 if out.dtype == torch.float32 else W12_Y_BF16
+    need = gemm_workspace_bytes(pw.n, pw.k, m)
+    if ws is None:
+        ws = workspace(need, x.device)
+    d = pw.desc()
+    _ok(lib().w12_gemm(ctypes.byref(d), _ptr(x), m, _ptr(out), yt, _ptr(ws), ws.numel(),
+                       _stream(x.device)), "w12_gemm")
+    return out
+
+
+def w12_head_argmax(pw: PackedW12, x: torch.Tensor, ws: torch.Tensor | None = None,
+                    with_max: bool = True):
+    """Greedy token per row: (idx int32 [m], max logit float32 [m] or None)."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if k != pw.k:
+        raise ValueError(f"x has k={k}, head has k={pw.k}")
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    mx = torch.empty(m, dtype=torch.float32, device=x.device) if with_max else None
+    need = ctypes.c_size_t(0)
+    _ok(lib().w12_head_argmax_workspace(pw.n, pw.k, m, ctypes.byref(need)),
+        "w12_head_argmax_workspace")
+    if ws is None:
+        ws = workspace(need.value, x.device, "head")
+    d = pw.desc()
+    _ok(lib().w12_head_argmax(ctypes.byref(d), _ptr(x), m, _ptr(idx), _ptr(mx), _ptr(ws),
+                              ws.numel(), _stream(x.device)), "w12_head_argmax")
+    return idx, mx
+
+
+def tree_accept(node_off: torch.Tensor, parent: torch.Tensor, token: torch.Tensor,
+                argmax: torch.Tensor):
+    """Greedy tree acceptance; returns (accept_len [T], path [sum n], bonus [T])."""
+    for t, nm in ((node_off, "node_off"), (parent, "parent"), (token, "token"),
+                  (argmax, "argmax")):
+        _need(t, torch.int32, nm, 1)
+    T = node_off.numel() - 1
+    total = parent.numel()
+    if T < 0 or token.numel() != total or argmax.numel() != total:
+        raise ValueError("tree_accept: inconsistent array sizes")
+    dev = parent.device
+    acc = torch.empty(max(T, 0), dtype=torch.int32, device=dev)
+    path = torch.empty(total, dtype=torch.int32, device=dev)
+    bonus = torch.empty(max(T, 0), dtype=torch.int32, device=dev)
+    _ok(lib().tree_accept(T, _ptr(node_off), total, _ptr(parent), _ptr(token), _ptr(argmax),
+                          _ptr(acc), _ptr(path), _ptr(bonus), _stream(dev)), "tree_accept")
+    return acc, path, bonus

@@ -1,0 +1,176 @@
+// extern "C" entry points of libw12 (declared in include/w12.h).
+//
+// Every call validates its arguments on the host and returns W12_EINVAL or
+// W12_ENOSPC before launching anything (the refusal-before-running style of
+// the poot-llm docs, "What is refused"), then enqueues its kernels on the
+// caller's stream. Nothing here allocates memory.
+#include <atomic>
+
+#include "../../include/w12.h"
+#include "w12_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxRows = 256;
+
+bool shape_ok(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0 || n % 32 != 0 || k % 256 != 0 || k > kMaxK) return false;
+  // escape offsets are u32: the weight count must fit
+  return n <= (int64_t(0xFFFFFFFF) / k);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool matrix_ok(const w12_matrix* w) {
+  return w && shape_ok(w->n, w->k) && w->records && w->e_top && w->esc_off && w->esc &&
+         aligned(w->records, 16) && aligned(w->esc_off, 4) && aligned(w->esc, 4);
+}
+
+w12::MatrixArgs args_of(const w12_matrix* w) {
+  w12::MatrixArgs a;
+  a.rec = w->records;
+  a.e_top = w->e_top;
+  a.esc_off = w->esc_off;
+  a.esc = w->esc;
+  a.n = w->n;
+  a.k = w->k;
+  a.nb = w->n * w->k / 1024;
+  return a;
+}
+
+// Compute-unit count of the current device, cached per device id.
+int num_cu() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return -1;
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+w12_status st(hipError_t e) { return e == hipSuccess ? W12_OK : W12_EHIP; }
+
+w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
+                    int32_t* idx, float* maxval, void* ws, size_t ws_bytes, hipStream_t s,
+                    int epi) {
+  const int cu = num_cu();
+  if (cu <= 0) return W12_EHIP;
+  const w12::GemmPlan pl = w12::plan_gemm(w->n, w->k, m, cu);
+  if (!ws || ws_bytes < pl.ws_bytes) return ws ? W12_ENOSPC : W12_EINVAL;
+  char* base = static_cast<char*>(ws);
+  w12::GemmParams p{};
+  p.w = args_of(w);
+  p.x = x;
+  p.M = (int)m;
+  p.N = (int)w->n;
+  p.K = (int)w->k;
+  p.RK = (int)(w->k / 256);
+  p.S = (int)(w->n / 32);
+  p.P = (p.S + 1) / 2;
+  p.U = p.P * p.RK;
+  p.G = pl.G;
+  p.y = y;
+  p.ytype = ytype;
+  p.part = reinterpret_cast<float*>(base + pl.off_part);
+  p.tile_cnt = reinterpret_cast<uint32_t*>(base + pl.off_cnt);
+  p.keys = reinterpret_cast<unsigned long long*>(base + pl.off_keys);
+  p.done = reinterpret_cast<uint32_t*>(base + pl.off_done);
+  p.idx = idx;
+  p.maxval = maxval;
+  return st(w12::launch_gemm(p, epi, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w12_strerror(int status) {
+  switch (status) {
+    case W12_OK: return "W12_OK";
+    case W12_EINVAL: return "W12_EINVAL: invalid argument";
+    case W12_ENOSPC: return "W12_ENOSPC: workspace too small";
+    case W12_EHIP: return "W12_EHIP: HIP runtime or launch error";
+    default: return "W12: unknown status";
+  }
+}
+
+int w12_abi_version(void) { return 1; }
+
+int64_t w12_num_blocks(int64_t n, int64_t k) {
+  if (!shape_ok(n, k)) return -1;
+  return n * k / 1024;
+}
+
+w12_status w12_pack_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top,
+                         uint32_t* esc_off, hipStream_t stream) {
+  if (!w || !e_top || !esc_off || !shape_ok(n, k) || !aligned(w, 16)) return W12_EINVAL;
+  return st(w12::launch_pack_plan(w, n, k, e_top, esc_off, stream));
+}
+
+w12_status w12_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top,
+                    const uint32_t* esc_off, uint8_t* records, uint32_t* esc,
+                    int64_t esc_capacity, hipStream_t stream) {
+  if (!w || !e_top || !esc_off || !records || !shape_ok(n, k) || esc_capacity < 0)
+    return W12_EINVAL;
+  if (!aligned(w, 16) || !aligned(records, 16)) return W12_EINVAL;
+  if (esc_capacity > 0 && !esc) return W12_EINVAL;
+  return st(w12::launch_pack(w, n, k, e_top, esc_off, records, esc, esc_capacity, stream));
+}
+
+w12_status w12_decode(const w12_matrix* w, uint16_t* out, hipStream_t stream) {
+  if (!matrix_ok(w) || !out || !aligned(out, 16)) return W12_EINVAL;
+  return st(w12::launch_decode(args_of(w), out, stream));
+}
+
+w12_status w12_check(const w12_matrix* w, const uint16_t* ref, unsigned long long* mismatches,
+                     hipStream_t stream) {
+  if (!matrix_ok(w) || !ref || !mismatches || !aligned(ref, 16)) return W12_EINVAL;
+  return st(w12::launch_check(args_of(w), ref, mismatches, stream));
+}
+
+w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
+  if (!bytes || !shape_ok(n, k) || m < 1 || m > kMaxRows) return W12_EINVAL;
+  const int cu = num_cu();
+  if (cu <= 0) return W12_EHIP;
+  *bytes = w12::plan_gemm(n, k, m, cu).ws_bytes;
+  return W12_OK;
+}
+
+w12_status w12_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!matrix_ok(w) || !x || !y || m < 1 || m > kMaxRows) return W12_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return W12_EINVAL;
+  if (ytype != W12_Y_F32 && ytype != W12_Y_BF16) return W12_EINVAL;
+  return run_gemm(w, x, m, y, ytype, nullptr, nullptr, ws, ws_bytes, stream, w12::kEpiY);
+}
+
+w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
+  return w12_gemm_workspace(n, k, m, bytes);
+}
+
+w12_status w12_head_argmax(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,
+                           float* maxval, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!matrix_ok(head) || !x || !idx || m < 1 || m > kMaxRows) return W12_EINVAL;
+  if (!aligned(x, 16)) return W12_EINVAL;
+  return run_gemm(head, x, m, nullptr, 0, idx, maxval, ws, ws_bytes, stream, w12::kEpiArgmax);
+}
+
+w12_status tree_accept(int32_t num_trees, const int32_t* node_off, int32_t total_nodes,
+                       const int32_t* parent, const int32_t* token, const int32_t* argmax,
+                       int32_t* accept_len, int32_t* path, int32_t* bonus, hipStream_t stream) {
+  if (num_trees < 0 || total_nodes < 0) return W12_EINVAL;
+  if (num_trees == 0) return W12_OK;
+  if (!node_off || !accept_len || !bonus) return W12_EINVAL;
+  if (total_nodes > 0 && (!parent || !token || !argmax || !path)) return W12_EINVAL;
+  return st(w12::launch_tree_accept(num_trees, node_off, total_nodes, parent, token, argmax,
+                                    accept_len, path, bonus, stream));
+}
+
+}  // extern "C"

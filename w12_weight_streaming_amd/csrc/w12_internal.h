@@ -1,0 +1,63 @@
+// Host-side launch interface between the C ABI (w12_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w12 {
+
+struct MatrixArgs {
+  const uint8_t* rec;
+  const uint8_t* e_top;
+  const uint32_t* esc_off;
+  const uint32_t* esc;
+  int64_t n, k, nb;
+};
+
+enum Epilogue { kEpiY = 0, kEpiArgmax = 1 };
+
+// One verify GEMM (or LM head) launch. Work is split stream-K style: a unit
+// is one record of a 64-channel tile (two 32-channel strips), units run
+// tile-major, and workgroup g owns units [g*U/G, (g+1)*U/G).
+struct GemmParams {
+  MatrixArgs w;
+  const uint16_t* x;
+  int M, N, K;
+  int RK;  // records per strip = K / 256
+  int S;   // strips = N / 32
+  int P;   // tiles = ceil(S / 2)
+  int U;   // units = P * RK
+  int G;   // workgroups
+  void* y;
+  int ytype;
+  float* part;            // [2G][M][64] split-tile partial sums
+  uint32_t* tile_cnt;     // [P] arrival counters, zero between calls
+  unsigned long long* keys;  // [M] argmax keys, zero between calls
+  uint32_t* done;         // [1] finished-workgroup counter, zero between calls
+  int32_t* idx;
+  float* maxval;
+};
+
+struct GemmPlan {
+  int G;
+  size_t ws_bytes;
+  size_t off_cnt, off_part, off_keys, off_done;
+};
+
+GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu);
+
+hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s);
+
+hipError_t launch_pack_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top,
+                            uint32_t* esc_off, hipStream_t s);
+hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top,
+                       const uint32_t* esc_off, uint8_t* rec, uint32_t* esc, int64_t cap,
+                       hipStream_t s);
+hipError_t launch_decode(const MatrixArgs& a, uint16_t* out, hipStream_t s);
+hipError_t launch_check(const MatrixArgs& a, const uint16_t* ref, unsigned long long* mism,
+                        hipStream_t s);
+hipError_t launch_tree_accept(int32_t num_trees, const int32_t* node_off, int32_t total,
+                              const int32_t* parent, const int32_t* token, const int32_t* argmax,
+                              int32_t* accept_len, int32_t* path, int32_t* bonus, hipStream_t s);
+
+}  // namespace w12

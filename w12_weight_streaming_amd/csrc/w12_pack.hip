@@ -1,0 +1,302 @@
+// W12 packing, decode and load-time check kernels (gfx950).
+//
+// Packing happens once, when the weights are loaded ("SpecPilot ..."
+// summary, section 4.1: weights are converted and the restored tensors are
+// checked bit-for-bit against the checkpoint at load time). The flow:
+//   window_kernel  per-channel exponent histogram -> window top E_n
+//   count_kernel   escapes per 32-channel x 32-k block
+//   scan_kernel    exclusive scan of the counts -> esc_off
+//   encode_kernel  records (8-bit view + low nibbles) and escape entries
+//   decode_kernel  the GEMM's in-register restore + escape patch, to bf16
+//                  (w12_decode) or compared against the source (w12_check)
+#include "w12_device.h"
+#include "w12_internal.h"
+
+namespace w12 {
+
+namespace {
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const unsigned long long w = ((unsigned long long)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Branch-free on purpose (bitwise &, selects below): every lane computes the
+// same instruction stream, so no value depends on divergent-path lowering.
+__device__ __forceinline__ uint32_t in_window(uint32_t b, uint32_t top) {
+  const uint32_t e = (b >> 7) & 0xFFu;
+  return (uint32_t)(e >= 1u) & (uint32_t)(e <= 254u) & (uint32_t)(e + 15u >= top) &
+         (uint32_t)(e <= top);
+}
+
+// 16 bf16 of one row: the lane's weights of a 32-channel x 32-k block.
+__device__ __forceinline__ void load16(const uint16_t* p, uint32_t (&b)[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 c = *reinterpret_cast<const uint4*>(p + 8);
+  const uint32_t d[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    b[2 * i] = d[i] & 0xFFFFu;
+    b[2 * i + 1] = d[i] >> 16;
+  }
+}
+
+struct BlockPos {
+  int64_t s, r, t;
+  int c, h;
+  int64_t n, k0;
+};
+
+__device__ __forceinline__ BlockPos block_pos(int64_t b, int64_t RK, int lane) {
+  BlockPos q;
+  q.s = b / (RK * 8);
+  q.r = (b / 8) % RK;
+  q.t = b % 8;
+  q.c = lane & 31;
+  q.h = lane >> 5;
+  q.n = q.s * kStrip + q.c;
+  q.k0 = q.r * kRecK + q.t * kSubK + 16 * q.h;
+  return q;
+}
+
+// One wavefront per channel: histogram of normal exponents, then the window
+// top holding the most of them (smallest top on ties), in [16, 254].
+__global__ __launch_bounds__(256) void window_kernel(const uint16_t* __restrict__ w, int64_t N,
+                                                     int64_t K, uint8_t* __restrict__ e_top) {
+  __shared__ uint32_t hist[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+  wave_lds_sync();
+  if (n < N) {
+    const uint4* row = reinterpret_cast<const uint4*>(w + n * K);
+    for (int64_t i = lane; i < K / 8; i += 64) {
+      const uint4 v = row[i];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t b = (q & 1) ? (d[q >> 1] >> 16) : (d[q >> 1] & 0xFFFFu);
+        const uint32_t e = (b >> 7) & 0xFFu;
+        if (e >= 1u && e <= 254u) atomicAdd(&hist[wave][e], 1u);
+      }
+    }
+  }
+  wave_lds_sync();
+  unsigned long long best = 0;
+  for (int E = 16 + lane; E <= 254; E += 64) {
+    uint32_t cov = 0;
+    for (int e = E - 15; e <= E; ++e) cov += hist[wave][e];
+    const unsigned long long key = ((unsigned long long)cov << 8) | (uint32_t)(255 - E);
+    best = key > best ? key : best;
+  }
+  best = wave_max_u64(best);
+  if (lane == 0 && n < N) e_top[n] = (uint8_t)(255u - (uint32_t)(best & 0xFFu));
+}
+
+// One wavefront per escape block: number of weights outside the window.
+__global__ __launch_bounds__(256) void count_kernel(const uint16_t* __restrict__ w, int64_t K,
+                                                    const uint8_t* __restrict__ e_top,
+                                                    uint32_t* __restrict__ counts, int64_t NB) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+  if (b >= NB) return;
+  const BlockPos q = block_pos(b, K / kRecK, lane);
+  uint32_t bits[16];
+  load16(w + q.n * K + q.k0, bits);
+  const uint32_t top = e_top[q.n];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) cnt += 1u - in_window(bits[j], top);
+  cnt = wave_sum_u32(cnt);
+  if (lane == 0) counts[b] = cnt;
+}
+
+// Single workgroup, in place: a[0..NB) counts -> exclusive offsets, a[NB] = total.
+__global__ __launch_bounds__(1024) void scan_kernel(uint32_t* __restrict__ a, int64_t NB) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (NB + 1023) / 1024;
+  const int64_t begin = min(NB, tid * per), end = min(NB, begin + per);
+  uint32_t sum = 0;
+  for (int64_t i = begin; i < end; ++i) sum += a[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = part[tid] - sum;
+  for (int64_t i = begin; i < end; ++i) {
+    const uint32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == 1023) a[NB] = part[1023];
+}
+
+// One wavefront per escape block: codes into the record, escapes into the
+// block's slice of `esc` in (channel, k) order.
+__global__ __launch_bounds__(256) void encode_kernel(const uint16_t* __restrict__ w, int64_t K,
+                                                     const uint8_t* __restrict__ e_top,
+                                                     const uint32_t* __restrict__ esc_off,
+                                                     uint8_t* __restrict__ rec,
+                                                     uint32_t* __restrict__ esc, int64_t cap,
+                                                     int64_t NB) {
+  __shared__ uint32_t cnt_s[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+  if (b >= NB) return;
+  const int64_t RK = K / kRecK;
+  const BlockPos q = block_pos(b, RK, lane);
+  uint32_t bits[16];
+  load16(w + q.n * K + q.k0, bits);
+  const uint32_t top = e_top[q.n];
+  uint32_t hi8[16], lo4[16];
+  uint32_t escmask = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t x = bits[j];
+    const uint32_t keep = 0u - in_window(x, top);  // all ones when coded in the window
+    const uint32_t s = x >> 15, e = (x >> 7) & 0xFFu, m = x & 0x7Fu;
+    const uint32_t o = (e + 15u - top) & 15u;
+    hi8[j] = ((s << 7) | (o << 3) | (m >> 4)) & keep;
+    lo4[j] = (m & 15u) & keep;
+    escmask |= (~keep & 1u) << j;
+  }
+  uint32_t hw[4], lw[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    hw[i] = hi8[4 * i] | (hi8[4 * i + 1] << 8) | (hi8[4 * i + 2] << 16) | (hi8[4 * i + 3] << 24);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) v |= ((lo4[8 * d + bb] << 4) | lo4[8 * d + 4 + bb]) << (8 * bb);
+    lw[d] = v;
+  }
+  const int64_t rb = (q.s * RK + q.r) * kRecBytes;
+  *reinterpret_cast<uint4*>(rec + rb + q.t * 1024 + lane * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  *reinterpret_cast<uint2*>(rec + rb + kHiBytes + q.t * 512 + lane * 8) = make_uint2(lw[0], lw[1]);
+
+  // entries ordered by (c, kk): lane (c, h) comes at position 2c + h
+  const uint32_t cnt = __builtin_popcount(escmask);
+  const int key = 2 * q.c + q.h;
+  cnt_s[wave][key] = cnt;
+  wave_lds_sync();
+  uint32_t prefix = 0;
+  for (int i = 0; i < key; ++i) prefix += cnt_s[wave][i];
+  int64_t idx = (int64_t)esc_off[b] + prefix;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (escmask & (1u << j)) {
+      if (idx < cap)
+        esc[idx] = (bits[j] << 16) | ((uint32_t)q.c << 5) | (uint32_t)(16 * q.h + j);
+      ++idx;
+    }
+  }
+}
+
+// One wavefront per escape block: restore exactly as the GEMM does (decode16
+// then the escape patch through LDS), then store or compare.
+template <bool kCheck>
+__global__ __launch_bounds__(256) void decode_kernel(MatrixArgs a, uint16_t* __restrict__ out,
+                                                     const uint16_t* __restrict__ ref,
+                                                     unsigned long long* __restrict__ mism) {
+  __shared__ uint32_t buf[4][512];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+  if (b >= a.nb) return;
+  const int64_t RK = a.k / kRecK;
+  const BlockPos q = block_pos(b, RK, lane);
+  const int64_t rb = (q.s * RK + q.r) * kRecBytes;
+  const uint4 hi = *reinterpret_cast<const uint4*>(a.rec + rb + q.t * 1024 + lane * 16);
+  const uint2 lo = *reinterpret_cast<const uint2*>(a.rec + rb + kHiBytes + q.t * 512 + lane * 8);
+  uint32_t p[8];
+  decode16(hi, lo, bias2_of(a.e_top[q.n]), p);
+  const uint32_t o = a.esc_off[b];
+  const uint32_t cnt = a.esc_off[b + 1] - o;
+  if (cnt) {
+    uint32_t* wb = buf[wave];
+    *reinterpret_cast<uint4*>(wb + lane * 8) = make_uint4(p[0], p[1], p[2], p[3]);
+    *reinterpret_cast<uint4*>(wb + lane * 8 + 4) = make_uint4(p[4], p[5], p[6], p[7]);
+    wave_lds_sync();
+    for (uint32_t i = lane; i < cnt; i += 64) {
+      const uint32_t e = a.esc[o + i];
+      const uint32_t owner = esc_c(e) + ((esc_kk(e) >> 4) << 5);
+      reinterpret_cast<uint16_t*>(wb + owner * 8)[esc_kk(e) & 15u] = esc_bits(e);
+    }
+    wave_lds_sync();
+    const uint4 r0 = *reinterpret_cast<const uint4*>(wb + lane * 8);
+    const uint4 r1 = *reinterpret_cast<const uint4*>(wb + lane * 8 + 4);
+    p[0] = r0.x; p[1] = r0.y; p[2] = r0.z; p[3] = r0.w;
+    p[4] = r1.x; p[5] = r1.y; p[6] = r1.z; p[7] = r1.w;
+  }
+  if constexpr (!kCheck) {
+    uint4* dst = reinterpret_cast<uint4*>(out + q.n * a.k + q.k0);
+    dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
+    dst[1] = make_uint4(p[4], p[5], p[6], p[7]);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(ref + q.n * a.k + q.k0);
+    const uint4 r0 = src[0], r1 = src[1];
+    const uint32_t rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    uint32_t bad = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t d = p[i] ^ rr[i];
+      bad += ((d & 0xFFFFu) != 0) + ((d >> 16) != 0);
+    }
+    bad = wave_sum_u32(bad);
+    if (lane == 0 && bad) atomicAdd(mism, (unsigned long long)bad);
+  }
+}
+
+inline unsigned grid_for(int64_t waves) { return (unsigned)((waves + 3) / 4); }
+
+}  // namespace
+
+hipError_t launch_pack_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top,
+                            uint32_t* esc_off, hipStream_t s) {
+  const int64_t nb = n * k / 1024;
+  hipLaunchKernelGGL(window_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, n, k, e_top);
+  hipLaunchKernelGGL(count_kernel, dim3(grid_for(nb)), dim3(256), 0, s, w, k, e_top, esc_off, nb);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, esc_off, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top,
+                       const uint32_t* esc_off, uint8_t* rec, uint32_t* esc, int64_t cap,
+                       hipStream_t s) {
+  const int64_t nb = n * k / 1024;
+  hipLaunchKernelGGL(encode_kernel, dim3(grid_for(nb)), dim3(256), 0, s, w, k, e_top, esc_off,
+                     rec, esc, cap, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const MatrixArgs& a, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(decode_kernel<false>, dim3(grid_for(a.nb)), dim3(256), 0, s, a, out,
+                     (const uint16_t*)nullptr, (unsigned long long*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_check(const MatrixArgs& a, const uint16_t* ref, unsigned long long* mism,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(decode_kernel<true>, dim3(grid_for(a.nb)), dim3(256), 0, s, a,
+                     (uint16_t*)nullptr, ref, mism);
+  return hipGetLastError();
+}
+
+}  // namespace w12
