@@ -23,8 +23,8 @@
  *     stream) and return as soon as the kernels are enqueued.
  *   - Argument errors return W12_EINVAL before anything is launched (null
  *     pointers, shapes the format cannot hold, m outside [1, 256], bf16
- *     matrices / records / x / y not 16-byte aligned, u32 arrays not 4-byte
- *     aligned); a
+ *     matrices / records / x / y not 16-byte aligned, e_top and u32 arrays
+ *     not 4-byte aligned); a
  *     workspace smaller than its query returns W12_ENOSPC; a failed launch
  *     returns W12_EHIP.  Errors found on the device (a corrupt packed
  *     weight, an invalid tree) are reported through outputs, as each call
@@ -53,7 +53,8 @@
  *              code 0 and are listed in `esc`.
  *   esc_off    [N*K/1024 + 1] u32 offsets into esc, one per escape block
  *              (strip s, record r, subtile t), block id (s*(K/256)+r)*8 + t.
- *   esc        [esc_off[last]] u32 entries bits<<16 | c<<5 | kk, c the
+ *   esc        [max(1, esc_off[last])] u32 entries (the array always holds
+ *              at least one element) bits<<16 | c<<5 | kk, c the
  *              channel in the strip, kk = k % 32; (c, kk) ascending within a
  *              block, so each channel's list runs in ascending k.
  */

@@ -24,7 +24,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool matrix_ok(const w12_matrix* w) {
   return w && shape_ok(w->n, w->k) && w->records && w->e_top && w->esc_off && w->esc &&
-         aligned(w->records, 16) && aligned(w->esc_off, 4) && aligned(w->esc, 4);
+         aligned(w->records, 16) && aligned(w->e_top, 4) && aligned(w->esc_off, 4) &&
+         aligned(w->esc, 4);
 }
 
 w12::MatrixArgs args_of(const w12_matrix* w) {
