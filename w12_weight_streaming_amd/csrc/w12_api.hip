@@ -80,6 +80,7 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
   p.y = y;
   p.ytype = ytype;
   p.part = reinterpret_cast<float*>(base + pl.off_part);
+  p.xf = reinterpret_cast<uint4*>(base + pl.off_xf);
   p.tile_cnt = reinterpret_cast<uint32_t*>(base + pl.off_cnt);
   p.keys = reinterpret_cast<unsigned long long*>(base + pl.off_keys);
   p.done = reinterpret_cast<uint32_t*>(base + pl.off_done);

@@ -3,27 +3,34 @@
 // What is computed ("SpecPilot ..." summary, section 4.1): the verify pass
 // multiplies every target linear layer, restored from W12 records in
 // registers, against the handful of draft-tree rows in one weight read; the
-// split of the k reduction across workgroups runs in a fixed order, so the
-// GEMM is deterministic. The LM head variant keeps the logits in registers
-// and emits only the greedy token (section 1.1: the target's argmax).
+// k reduction is split across workgroups in a fixed order, so the GEMM is
+// deterministic. The LM-head variant keeps the logits in registers and emits
+// only the greedy token (section 1.1: the target's argmax).
 //
-// gfx950 design:
-//  * A work unit is one record (256 k) of a 64-channel tile (a pair of
-//    32-channel strips). Units run tile-major; workgroup g owns a contiguous
-//    slice of them (stream-K). A tile that straddles slices is finished by
-//    whichever contributor arrives last, summing the slices' partials in
-//    slice order.
-//  * Inside a workgroup, wave w handles subtiles t = w, w + NW, ... (32 k each)
-//    of every unit, so the eight 1.5 KB pieces of a 12 KB record are read by
-//    different waves with one 16-byte + one 8-byte load per lane.
-//  * Each lane restores its 16 weights in registers (decode16), escapes are
-//    patched through a per-wave LDS buffer, then:
-//      m >= 16: bf16 MFMA 32x32x16; the lane's 16 weights are two A
-//               fragments, x is the B operand (m = lane % 32);
-//      m <  16: lanes own channels, fdot2 against x broadcast to the wave.
-//  * Loads run two units ahead of the arithmetic (three register stages).
-#include <utility>
+// gfx950 design (HBM-bound at every m this kernel serves):
+//  * Tile = 64 output channels (a pair of 32-channel strips). Unit = one
+//    256-k record of a tile (2 x 12 KB). Units run tile-major; workgroup g
+//    owns the contiguous slice [g*U/G, (g+1)*U/G) (stream-K). A tile split
+//    between slices is finished by the last contributor to arrive, which sums
+//    the slices' partials in slice order.
+//  * 8 waves per workgroup; wave w restores subtile w (32 k) of both strips of
+//    every unit: per lane one 16-byte load of the 8-bit view and one 8-byte
+//    load of the low nibbles per strip, nontemporal, through raw buffer
+//    resources (loads past a slice's end use an empty resource: no traffic).
+//  * Loads run D units ahead of the arithmetic and are always issued
+//    unconditionally; the loop has no barrier that waits on vector memory,
+//    so the next units' loads stay in flight across every barrier.
+//  * m >= 16: bf16 MFMA 32x32x16, weights = A, x = B. The B fragments come
+//    from a copy of x rearranged once per call so that every fragment load
+//    is one contiguous 1 KB per wave (xfrag_kernel).
+//  * m < 16: lanes own channels, fdot2 against x rows read from memory
+//    (all lanes of a half-wave read the same 16 bytes).
+//  * Escapes (~1% of weights here): restored pairs go through a per-wave LDS
+//    buffer, the lanes holding the block's escape entries overwrite their
+//    slots, and the pairs are read back -- all synchronised within the wave.
+#include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "w12_device.h"
 #include "w12_internal.h"
@@ -33,9 +40,23 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kNW = 8;                          // waves per workgroup (= subtiles per record)
+constexpr int kNT = kNW * 64;
+constexpr int kRedStride = 68;                  // floats per 64-channel row (+4 pad)
+constexpr int kSlotFloats = 32 * kRedStride;    // one 32-row x 64-channel reduction slot
+constexpr int kLdsFloats = 4 * kSlotFloats;     // 34816 B >= 8 waves x 4 KB of patch buffers
+constexpr int kRawBufferWord3 = 0x00020000;     // gfx9-family raw buffer descriptor word 3
+constexpr int kNonTemporal = 2;                 // load cache policy: streaming
+
+#ifndef W12_PIPE_DEPTH
+#define W12_PIPE_DEPTH 2
+#endif
+constexpr int kDepth = W12_PIPE_DEPTH;          // units of weight loads in flight per wave
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 with constant i, so
-// register arrays indexed by i stay in registers even across barriers.
+// arrays of load slots indexed by i stay in registers.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -45,11 +66,51 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-constexpr int kRedStride = 68;                  // floats per 64-channel row (+4 pad)
-constexpr int kSlotFloats = 32 * kRedStride;    // one 32-row x 64-channel slot
-constexpr int kLdsFloats = 4 * kSlotFloats;     // 34816 B >= 8 waves x 4 KB patch
+// Buffer resource from wave-uniform base and size. The fields pass through
+// readfirstlane so the descriptor is built in scalar registers even where the
+// compiler would otherwise materialise a uniform select in vector registers
+// (a descriptor in vector registers turns every load into a waterfall loop).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           kRawBufferWord3);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, AUX));
+}
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
 
-// Dispatch sends workgroup b to XCD b % 8. Renumber so that each XCD gets a
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS
+// operations, never for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Ordering point between LDS writes of one lane and reads of another lane of
+// the same wave: a wave's LDS operations execute in issue order, so only the
+// compiler has to be kept from reordering them.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Dispatch sends workgroup b to XCD b % 8. Renumber so that each XCD runs a
 // contiguous run of slices: neighbours that share a split tile then share an
 // L2 as well.
 __device__ __forceinline__ int logical_wg(int b, int G) {
@@ -62,20 +123,13 @@ __device__ __forceinline__ int chunk_begin(int g, int U, int G) {
 __device__ __forceinline__ int owner_of(int u, int U, int G) {
   return (int)(((int64_t)(u + 1) * G + U - 1) / U) - 1;
 }
+// Partial-sum slot of workgroup g for tile p: its first tile or its last.
 __device__ __forceinline__ int partial_slot(int g, int p, int U, int G, int RK) {
   return (p == chunk_begin(g, U, G) / RK) ? 2 * g : 2 * g + 1;
 }
 
-template <typename T>
-__device__ __forceinline__ T stream_load(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-}
-
-__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// Final value of 4 consecutive channels (n .. n+3) of row m.
+// Final value of 4 consecutive channels (n .. n+3) of row m. For the argmax
+// epilogue, 16 consecutive threads of a wave hold one row's 64 channels.
 template <int EPI>
 __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n, float4 v) {
   const bool valid = m < a.M && n < a.N;
@@ -108,16 +162,43 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
       const unsigned long long w = ((unsigned long long)hi << 32) | lo;
       best = w > best ? w : best;
     }
-    if ((tid & 15) == 0 && valid && best) atomicMax(&a.keys[m], best);
+    if ((tid & 15) == 0 && best) atomicMax(&a.keys[m], best);
   }
+}
+
+// Cross-workgroup hand-off without a device-scope fence. A device-scope
+// fence on gfx950 writes back and invalidates the whole L2 of the XCD, which
+// every workgroup sharing that L2 then pays for (the x fragments and escape
+// metadata are L2-resident). Instead, partial sums are stored write-through
+// at device scope (sc1), each thread waits until its own stores are
+// acknowledged, the workgroup synchronises, and only then one thread bumps
+// the device-coherent arrival counter. The last contributor reads the partials
+// with device-scope loads that bypass its L2, so it cannot see stale lines.
+constexpr int kDeviceScope = 16;  // sc1 cache-policy bit: coherent across XCDs
+
+__device__ __forceinline__ void store_partial(const GemmParams& a, int slot, int m, int c4, float4 v) {
+  const rsrc_t r = make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
+  const u32x4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, (uint32_t)((slot * a.M + m) * 64 + c4) * 4u, 0, kDeviceScope);
+}
+__device__ __forceinline__ float4 load_partial(const GemmParams& a, int slot, int m, int c4) {
+  const rsrc_t r = make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
+  const u32x4 d = bload4<kDeviceScope>(r, (uint32_t)((slot * a.M + m) * 64 + c4) * 4u, 0);
+  return make_float4(__uint_as_float(d.x), __uint_as_float(d.y), __uint_as_float(d.z), __uint_as_float(d.w));
+}
+// Every thread's earlier global writes and atomics are acknowledged, then
+// the workgroup synchronises.
+__device__ __forceinline__ void writes_done_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
 }
 
 // Last contributor of a split tile sums the partials in slice order.
 template <int EPI>
-__device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, int tid, int nthreads,
-                                                  int* s_last) {
-  __threadfence();
-  __syncthreads();
+__device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_last) {
+  writes_done_barrier();
   const int gf = owner_of(p * a.RK, a.U, a.G);
   const int gl = owner_of((p + 1) * a.RK - 1, a.U, a.G);
   if (tid == 0) {
@@ -126,13 +207,11 @@ __device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, in
   }
   __syncthreads();
   if (*s_last) {
-    __threadfence();
-    for (int e = tid; e < a.M * 16; e += nthreads) {
+    for (int e = tid; e < ((a.M + 31) & ~31) * 16; e += kNT) {
       const int m = e >> 4, c4 = (e & 15) * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int gg = gf; gg <= gl; ++gg) {
-        const int sl = partial_slot(gg, p, a.U, a.G, a.RK);
-        v = f4add(v, *reinterpret_cast<const float4*>(a.part + ((int64_t)sl * a.M + m) * 64 + c4));
+      if (m < a.M) {
+        for (int gg = gf; gg <= gl; ++gg) v = f4add(v, load_partial(a, partial_slot(gg, p, a.U, a.G, a.RK), m, c4));
       }
       emit4<EPI>(a, tid, m, p * 64 + c4, v);
     }
@@ -141,17 +220,17 @@ __device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, in
   __syncthreads();
 }
 
-// After the whole grid is done, the last workgroup turns keys into ids.
+// After the whole grid is done, the last workgroup turns keys into ids and
+// returns the keys and the done counter to zero (keys are read and cleared
+// with device-coherent atomics).
 template <int EPI>
-__device__ __forceinline__ void finish_grid(const GemmParams& a, int tid, int nthreads, int* s_last) {
+__device__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
   if constexpr (EPI == kEpiArgmax) {
-    __threadfence();
-    __syncthreads();
+    writes_done_barrier();
     if (tid == 0) *s_last = (atomicAdd(a.done, 1u) == (uint32_t)(a.G - 1)) ? 1 : 0;
     __syncthreads();
     if (*s_last) {
-      __threadfence();
-      for (int m = tid; m < a.M; m += nthreads) {
+      for (int m = tid; m < a.M; m += kNT) {
         const unsigned long long k = atomicExch(&a.keys[m], 0ull);
         a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
         if (a.maxval) a.maxval[m] = key_float((uint32_t)(k >> 32));
@@ -161,62 +240,90 @@ __device__ __forceinline__ void finish_grid(const GemmParams& a, int tid, int nt
   }
 }
 
-// Escape offsets of the units [wbase, wbase + 64) held one unit per lane.
-template <int TPW, int NW>
-__device__ __forceinline__ void load_offsets(const GemmParams& a, int wbase, int u1, int wave,
-                                             int lane, uint32_t (&off)[TPW][4]) {
-  const int u = wbase + lane;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) off[i][0] = off[i][1] = off[i][2] = off[i][3] = 0;
-  if (u < u1) {
-    const int p = u / a.RK, r = u - p * a.RK;
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + NW * i;
-      const int64_t b0 = ((int64_t)(2 * p) * a.RK + r) * 8 + t;
-      off[i][0] = a.w.esc_off[b0];
-      off[i][1] = a.w.esc_off[b0 + 1];
-      if (2 * p + 1 < a.S) {
-        const int64_t b1 = b0 + (int64_t)a.RK * 8;
-        off[i][2] = a.w.esc_off[b1];
-        off[i][3] = a.w.esc_off[b1 + 1];
-      }
-    }
-  }
+// Window top of this lane's channel from the dword holding it (channel index
+// = 4j + (lane & 3) within every strip).
+__device__ __forceinline__ uint32_t etop_byte(uint32_t dw, int lane) {
+  return (dw >> (8 * (lane & 3))) & 0xFFu;
 }
 
-__device__ __forceinline__ void patch_entry(uint32_t* buf, uint32_t e, int owner_base) {
-  const uint32_t kk = esc_kk(e);
-  reinterpret_cast<uint16_t*>(buf + (owner_base + esc_c(e) + ((kk >> 4) << 5)) * 8)[kk & 15u] =
-      esc_bits(e);
+// Per-wave patch buffer of one strip: 2 KB = [k half j/8][lane][4 dwords], so
+// each 16-byte LDS access of the wave covers consecutive addresses.
+__device__ __forceinline__ void patch_store(uint32_t* buf, int lane, const uint32_t (&p)[8]) {
+  *reinterpret_cast<uint4*>(buf + lane * 4) = make_uint4(p[0], p[1], p[2], p[3]);
+  *reinterpret_cast<uint4*>(buf + 256 + lane * 4) = make_uint4(p[4], p[5], p[6], p[7]);
 }
+__device__ __forceinline__ void patch_load(const uint32_t* buf, int lane, uint32_t (&p)[8]) {
+  const uint4 r0 = *reinterpret_cast<const uint4*>(buf + lane * 4);
+  const uint4 r1 = *reinterpret_cast<const uint4*>(buf + 256 + lane * 4);
+  p[0] = r0.x; p[1] = r0.y; p[2] = r0.z; p[3] = r0.w;
+  p[4] = r1.x; p[5] = r1.y; p[6] = r1.z; p[7] = r1.w;
+}
+// Overwrite one restored weight with an escape entry (bits << 16 | c << 5 |
+// kk): it sits at position kk % 16 of lane c + 32 (kk / 16).
+__device__ __forceinline__ void patch_put(uint32_t* buf, uint32_t e) {
+  const uint32_t kk = esc_kk(e), owner = esc_c(e) + ((kk >> 4) << 5), j = kk & 15u;
+  reinterpret_cast<uint16_t*>(buf + (j >> 3) * 256 + owner * 4)[j & 7u] = esc_bits(e);
+}
+
+// Position in a workgroup's slice of units.
+struct UnitIt {
+  int u, p, r;
+  __device__ __forceinline__ void init(int u0, int RK) {
+    u = u0;
+    p = u0 / RK;
+    r = u0 - p * RK;
+  }
+  __device__ __forceinline__ void next(int RK) {
+    ++u;
+    if (++r == RK) {
+      r = 0;
+      ++p;
+    }
+  }
+};
+
+// One unit's loads for one wave (subtile t = wave of both strips).
+template <int XQ>
+struct Slot {
+  uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
+  u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
+  u32x2 lo[2];         // their low nibbles
+  uint32_t et[2];      // dword holding the lane's channel's window top
+  uint32_t e[2];       // escape entry number `lane` of the block (if any)
+  u32x4 xv[XQ > 0 ? XQ : 1][2];  // x operands that ride with the unit
+};
+
+// Load ordering: vector loads of a wave return in issue order, so a wait for
+// one load is a wait for every older one. Per unit there are three groups:
+//   O  escape-block offsets           issued D + 1 units ahead
+//   W  records, window tops, x        issued D units ahead
+//   E  escape entries (address <- O)  issued D units ahead, after W
+// Issuing E(u + D) waits for O(u + D), sent one iteration earlier, which only
+// needs groups of units <= u + D - 1 to have arrived. So D units of weight
+// loads stay in flight during the arithmetic of a unit. The ring holds D + 2
+// slots: O runs one slot ahead of W/E, and one slot is being computed.
+template <int XQ>
+struct Ring {
+  static constexpr int NS = kDepth + 2;
+  Slot<XQ> s[NS];
+};
 
 // ============================================================================ MFMA path (m >= 16)
 
-template <int TPW, int XS>
-struct StageM {
-  u32x4 hi[TPW][2];
-  u32x2 lo[TPW][2];
-  uint32_t e[TPW][2];
-  int cnt[TPW][2];
-  uint32_t eb[TPW][2];
-  uint32_t bias[2];
-  u32x4 xv[TPW][XS > 0 ? XS : 1][2];
-};
-
-template <int MT, int NW, int EPI>
-__global__ __launch_bounds__(NW * 64) void gemm_mfma_kernel(GemmParams a) {
-  constexpr int TPW = 8 / NW;
-  constexpr int XS = MT <= 2 ? MT : 0;
-  constexpr int NT = NW * 64;
+template <int MT, int EPI>
+__global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
+  // x fragments for MT <= 2 tiles of 32 rows ride in the load ring; larger m
+  // loads them at the start of the unit (they are L2-resident).
+  constexpr int XQ = MT <= 2 ? MT : 0;
   __shared__ __align__(16) float lds[kLdsFloats];
   __shared__ int s_last;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = logical_wg(blockIdx.x, a.G);
-  const int u0 = chunk_begin(g, a.U, a.G), u1 = chunk_begin(g + 1, a.U, a.G);
-  const int RK = a.RK;
-  uint32_t* patch = reinterpret_cast<uint32_t*>(lds) + wave * (TPW * 1024);
+  const int U = a.U, RK = a.RK, S = a.S;
+  const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
+  uint32_t* patch = reinterpret_cast<uint32_t*>(lds) + wave * 1024;
 
   f32x16 acc[2][MT];
 #pragma unroll
@@ -226,72 +333,63 @@ __global__ __launch_bounds__(NW * 64) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  uint32_t off[TPW][4];
-  int wbase = u0;
-  load_offsets<TPW, NW>(a, wbase, u1, wave, lane, off);
+  const uint32_t tile_bytes = (uint32_t)RK * kRecBytes;  // one strip's records
+  const uint32_t eo_bytes = (uint32_t)((a.w.nb + 1) * 4);
+  const uint32_t xf_bytes = (uint32_t)(MT * 32) * (uint32_t)a.K * 2u;
+  const rsrc_t r_et = make_rsrc(a.w.e_top, (uint32_t)a.N);
+  const rsrc_t r_xf = make_rsrc(a.xf, xf_bytes);
+  const uint32_t v_hi = wave * 1024 + lane * 16;
+  const uint32_t v_lo = kHiBytes + wave * 512 + lane * 8;
+  const uint32_t v_et = (uint32_t)(lane & 28);
+  const uint32_t v_x = (uint32_t)lane * 16u;
 
-  // ---- loads for one unit
-  int nl = u0, lp = u0 / RK, lr = u0 - (u0 / RK) * RK;
-  auto load_next = [&](StageM<TPW, XS>& st) __attribute__((always_inline)) {
-    if (nl < u1) {
-      if (nl - wbase >= 64) {
-        wbase = nl;
-        load_offsets<TPW, NW>(a, wbase, u1, wave, lane, off);
-      }
-      const int li = nl - wbase;
-      const bool has1 = 2 * lp + 1 < a.S;
-      const uint8_t* rb0 = a.w.rec + ((int64_t)(2 * lp) * RK + lr) * kRecBytes;
-      const uint8_t* rb1 = rb0 + (int64_t)RK * kRecBytes;
+  auto issue_off = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
+    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
+    const u32x2 o0 = bload2(r, 0, b0 * 4);
+    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
+    s.off[0][0] = o0.x;
+    s.off[0][1] = o0.y;
+    s.off[1][0] = o1.x;
+    s.off[1][1] = o1.y;
+  };
+  auto issue_w = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const bool live = it.u < u1;
+    const bool has1 = 2 * it.p + 1 < S;
+    const uint32_t bytes = live ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
+    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * it.p) * tile_bytes, bytes);
+    const uint32_t so = (uint32_t)it.r * kRecBytes;
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int t = wave + NW * i;
-        st.hi[i][0] = stream_load<u32x4>(rb0 + t * 1024 + lane * 16);
-        st.lo[i][0] = stream_load<u32x2>(rb0 + kHiBytes + t * 512 + lane * 8);
-        if (has1) {
-          st.hi[i][1] = stream_load<u32x4>(rb1 + t * 1024 + lane * 16);
-          st.lo[i][1] = stream_load<u32x2>(rb1 + kHiBytes + t * 512 + lane * 8);
-        } else {
-          st.hi[i][1] = u32x4{0, 0, 0, 0};
-          st.lo[i][1] = u32x2{0, 0};
-        }
-        const uint32_t o0 = __builtin_amdgcn_readlane(off[i][0], li);
-        const uint32_t e0 = __builtin_amdgcn_readlane(off[i][1], li);
-        const uint32_t o1 = __builtin_amdgcn_readlane(off[i][2], li);
-        const uint32_t e1 = __builtin_amdgcn_readlane(off[i][3], li);
-        st.cnt[i][0] = (int)(e0 - o0);
-        st.cnt[i][1] = (int)(e1 - o1);
-        st.eb[i][0] = o0;
-        st.eb[i][1] = o1;
-        st.e[i][0] = lane < (int)(e0 - o0) ? a.w.esc[o0 + lane] : 0u;
-        st.e[i][1] = lane < (int)(e1 - o1) ? a.w.esc[o1 + lane] : 0u;
-        if constexpr (XS > 0) {
-          const int k0 = lr * kRecK + t * kSubK + 16 * (lane >> 5);
-#pragma unroll
-          for (int mt = 0; mt < XS; ++mt) {
-            const int m = mt * 32 + (lane & 31);
-            if (m < a.M) {
-              const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + (int64_t)m * a.K + k0);
-              st.xv[i][mt][0] = xp[0];
-              st.xv[i][mt][1] = xp[1];
-            } else {
-              st.xv[i][mt][0] = u32x4{0, 0, 0, 0};
-              st.xv[i][mt][1] = u32x4{0, 0, 0, 0};
-            }
-          }
-        }
-      }
-      const int n = lp * 64 + (lane & 31);
-      st.bias[0] = bias2_of(a.w.e_top[n]);
-      st.bias[1] = has1 ? bias2_of(a.w.e_top[n + 32]) : 0u;
+    for (int q = 0; q < 2; ++q) {
+      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
+      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
     }
-    ++nl;
-    if (++lr == RK) { lr = 0; ++lp; }
+    s.et[0] = bload1(r_et, v_et, (uint32_t)it.p * 64);
+    s.et[1] = bload1(r_et, v_et, (uint32_t)it.p * 64 + 32);
+    if constexpr (XQ > 0) {
+      const uint32_t b = (uint32_t)it.r * 8 + wave;
+      const rsrc_t rx = make_rsrc(a.xf, live ? xf_bytes : 0u);
+#pragma unroll
+      for (int mt = 0; mt < XQ; ++mt) {
+        s.xv[mt][0] = bload4(rx, v_x, ((b * MT + mt) * 2 + 0) * 1024);
+        s.xv[mt][1] = bload4(rx, v_x, ((b * MT + mt) * 2 + 1) * 1024);
+      }
+    }
+  };
+  auto issue_e = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const bool has1 = 2 * it.p + 1 < S;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = s.off[q][0];
+      const int c = (q == 0 || has1) ? (int)(s.off[q][1] - o) : 0;
+      s.e[q] = a.w.esc[c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u];
+    }
   };
 
-  // ---- tile flush: reduce the waves' accumulators, write or hand off
+  // ---- tile end: reduce the 8 waves' accumulators, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
     const bool whole = p * RK >= u0 && (p + 1) * RK <= u1;
-    const int slot = partial_slot(g, p, a.U, a.G, RK);
+    const int slot = partial_slot(g, p, U, a.G, RK);
     static_for<MT>([&](auto mtc) {
       constexpr int mt = decltype(mtc)::value;
       auto put = [&](float* dst, bool add) __attribute__((always_inline)) {
@@ -307,17 +405,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_mfma_kernel(GemmParams a) {
             *d = v;
           }
       };
-      __syncthreads();
-      if constexpr (NW == 8) {
-        if (wave >= 4) put(lds + (wave - 4) * kSlotFloats, false);
-        __syncthreads();
-        if (wave < 4) put(lds + wave * kSlotFloats, true);
-      } else {
-        put(lds + wave * kSlotFloats, false);
-      }
-      __syncthreads();
-      for (int e = tid; e < 32 * 16; e += NT) {
-        const int ml = e >> 4, c4 = (e & 15) * 4;
+      lds_barrier();
+      if (wave >= 4) put(lds + (wave - 4) * kSlotFloats, false);
+      lds_barrier();
+      if (wave < 4) put(lds + wave * kSlotFloats, true);
+      lds_barrier();
+      {
+        const int ml = tid >> 4, c4 = (tid & 15) * 4;  // 32 rows x 16 channel quads = kNT
         const float* b = lds + ml * kRedStride + c4;
         const float4 v = f4add(f4add(*reinterpret_cast<const float4*>(b),
                                      *reinterpret_cast<const float4*>(b + kSlotFloats)),
@@ -327,12 +421,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_mfma_kernel(GemmParams a) {
         if (whole) {
           emit4<EPI>(a, tid, m, p * 64 + c4, v);
         } else if (m < a.M) {
-          *reinterpret_cast<float4*>(a.part + ((int64_t)slot * a.M + m) * 64 + c4) = v;
+          store_partial(a, slot, m, c4, v);
         }
       }
     });
-    __syncthreads();
-    if (!whole) finish_split_tile<EPI>(a, p, tid, NT, &s_last);
+    lds_barrier();
+    if (!whole) finish_split_tile<EPI>(a, p, tid, &s_last);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -341,364 +435,416 @@ __global__ __launch_bounds__(NW * 64) void gemm_mfma_kernel(GemmParams a) {
         for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
   };
 
-  // ---- arithmetic for one unit
+  // ---- arithmetic of one unit
   int cp = u0 / RK, cr = u0 - (u0 / RK) * RK, tile = cp;
-  auto step = [&](const StageM<TPW, XS>& st) __attribute__((always_inline)) {
+  auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
     if (cp != tile) {
       flush(tile);
       tile = cp;
     }
-    const bool has1 = 2 * cp + 1 < a.S;
+    const bool has1 = 2 * cp + 1 < S;
+    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
+    const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
+    uint32_t P[2][8];
+    decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y},
+             bias2_of(etop_byte(s.et[0], lane)), P[0]);
+    decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y},
+             bias2_of(etop_byte(s.et[1], lane)), P[1]);
+    if (cnt0 + cnt1 > 0) {
+      patch_store(patch, lane, P[0]);
+      patch_store(patch + 512, lane, P[1]);
+      wave_lds_order();
+      const int cq[2] = {cnt0, cnt1};
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      uint32_t P[2][8];
-      decode16(uint4{st.hi[i][0].x, st.hi[i][0].y, st.hi[i][0].z, st.hi[i][0].w},
-               uint2{st.lo[i][0].x, st.lo[i][0].y}, st.bias[0], P[0]);
-      decode16(uint4{st.hi[i][1].x, st.hi[i][1].y, st.hi[i][1].z, st.hi[i][1].w},
-               uint2{st.lo[i][1].x, st.lo[i][1].y}, st.bias[1], P[1]);
-      if (st.cnt[i][0] + st.cnt[i][1] > 0) {
-        uint32_t* wb = patch + i * 1024;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          *reinterpret_cast<uint4*>(wb + q * 512 + lane * 8) = make_uint4(P[q][0], P[q][1], P[q][2], P[q][3]);
-          *reinterpret_cast<uint4*>(wb + q * 512 + lane * 8 + 4) = make_uint4(P[q][4], P[q][5], P[q][6], P[q][7]);
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (lane < st.cnt[i][q]) patch_entry(wb, st.e[i][q], q * 64);
-          for (int j = 64 + lane; j < st.cnt[i][q]; j += 64)
-            patch_entry(wb, a.w.esc[st.eb[i][q] + j], q * 64);
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint4 r0 = *reinterpret_cast<const uint4*>(wb + q * 512 + lane * 8);
-          const uint4 r1 = *reinterpret_cast<const uint4*>(wb + q * 512 + lane * 8 + 4);
-          P[q][0] = r0.x; P[q][1] = r0.y; P[q][2] = r0.z; P[q][3] = r0.w;
-          P[q][4] = r1.x; P[q][5] = r1.y; P[q][6] = r1.z; P[q][7] = r1.w;
-        }
+      for (int q = 0; q < 2; ++q) {
+        if (lane < cq[q]) patch_put(patch + q * 512, s.e[q]);
+        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 512, a.w.esc[s.off[q][0] + j]);
       }
-      const int t = wave + NW * i;
-      const int k0 = cr * kRecK + t * kSubK + 16 * (lane >> 5);
+      wave_lds_order();
+      patch_load(patch, lane, P[0]);
+      patch_load(patch + 512, lane, P[1]);
+    }
+    u32x4 xl[MT][2];
+    if constexpr (XQ > 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        u32x4 x0, x1;
-        if constexpr (XS > 0) {
-          x0 = st.xv[i][mt < XS ? mt : 0][0];
-          x1 = st.xv[i][mt < XS ? mt : 0][1];
-        } else {
-          const int m = mt * 32 + (lane & 31);
-          if (m < a.M) {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + (int64_t)m * a.K + k0);
-            x0 = xp[0];
-            x1 = xp[1];
-          } else {
-            x0 = u32x4{0, 0, 0, 0};
-            x1 = u32x4{0, 0, 0, 0};
-          }
-        }
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, x0);
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, x1);
-        const bf16x8 a00 = __builtin_bit_cast(bf16x8, u32x4{P[0][0], P[0][1], P[0][2], P[0][3]});
-        const bf16x8 a01 = __builtin_bit_cast(bf16x8, u32x4{P[0][4], P[0][5], P[0][6], P[0][7]});
-        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a00, b0, acc[0][mt], 0, 0, 0);
-        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a01, b1, acc[0][mt], 0, 0, 0);
-        if (has1) {
-          const bf16x8 a10 = __builtin_bit_cast(bf16x8, u32x4{P[1][0], P[1][1], P[1][2], P[1][3]});
-          const bf16x8 a11 = __builtin_bit_cast(bf16x8, u32x4{P[1][4], P[1][5], P[1][6], P[1][7]});
-          acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, b0, acc[1][mt], 0, 0, 0);
-          acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, b1, acc[1][mt], 0, 0, 0);
-        }
+        xl[mt][0] = s.xv[mt][0];
+        xl[mt][1] = s.xv[mt][1];
+      }
+    } else {
+      const uint32_t b = (uint32_t)cr * 8 + wave;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        xl[mt][0] = bload4(r_xf, v_x, ((b * MT + mt) * 2 + 0) * 1024);
+        xl[mt][1] = bload4(r_xf, v_x, ((b * MT + mt) * 2 + 1) * 1024);
       }
     }
-    if (++cr == RK) { cr = 0; ++cp; }
+    const bf16x8 a00 = __builtin_bit_cast(bf16x8, u32x4{P[0][0], P[0][1], P[0][2], P[0][3]});
+    const bf16x8 a01 = __builtin_bit_cast(bf16x8, u32x4{P[0][4], P[0][5], P[0][6], P[0][7]});
+    const bf16x8 a10 = __builtin_bit_cast(bf16x8, u32x4{P[1][0], P[1][1], P[1][2], P[1][3]});
+    const bf16x8 a11 = __builtin_bit_cast(bf16x8, u32x4{P[1][4], P[1][5], P[1][6], P[1][7]});
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, xl[mt][0]);
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, xl[mt][1]);
+      acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a00, b0, acc[0][mt], 0, 0, 0);
+      acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a01, b1, acc[0][mt], 0, 0, 0);
+      acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, b0, acc[1][mt], 0, 0, 0);
+      acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, b1, acc[1][mt], 0, 0, 0);
+    }
+    if (++cr == RK) {
+      cr = 0;
+      ++cp;
+    }
   };
 
   if (u0 < u1) {
-    StageM<TPW, XS> sA, sB, sC;
-    load_next(sA);
-    load_next(sB);
-    for (int u = u0; u < u1; u += 3) {
-      load_next(sC);
-      step(sA);
-      if (u + 1 >= u1) break;
-      load_next(sA);
-      step(sB);
-      if (u + 2 >= u1) break;
-      load_next(sB);
-      step(sC);
-    }
+    Ring<XQ> ring;
+    constexpr int NS = Ring<XQ>::NS;
+    UnitIt itO, itW;
+    itO.init(u0, RK);
+    itW.init(u0, RK);
+    issue_off(ring.s[0], itO);
+    itO.next(RK);
+    static_for<kDepth>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      issue_off(ring.s[j + 1], itO);
+      itO.next(RK);
+      issue_w(ring.s[j], itW);
+      issue_e(ring.s[j], itW);
+      itW.next(RK);
+    });
+    auto iteration = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      issue_off(ring.s[(k + kDepth + 1) % NS], itO);
+      itO.next(RK);
+      issue_w(ring.s[(k + kDepth) % NS], itW);
+      issue_e(ring.s[(k + kDepth) % NS], itW);
+      itW.next(RK);
+      step(ring.s[k]);
+    };
+    // Steady state without conditional steps: a skipped step inside the
+    // unrolled body would make the compiler's load-wait counts assume fewer
+    // loads in flight and wait for the next units' loads as well.
+    int base = u0;
+    for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
+    static_for<NS>([&](auto kc) {
+      if (base + decltype(kc)::value < u1) iteration(kc);
+    });
     flush(tile);
   }
-  finish_grid<EPI>(a, tid, NT, &s_last);
+  finish_grid<EPI>(a, tid, &s_last);
 }
 
 // ============================================================================ VALU path (m < 16)
 
-template <int XV>
-struct StageV {
-  u32x4 hi[2];       // [h]: k-half of the subtile; lane = channel of the tile
-  u32x2 lo[2];
-  uint32_t e[2];     // [q]: strip of the pair
-  int cnt[2];
-  uint32_t eb[2];
-  uint32_t bias;
-  u32x4 xv[2][XV > 0 ? XV : 1][2];
-};
-
 template <int MV, int EPI>
-__global__ __launch_bounds__(512) void gemm_valu_kernel(GemmParams a) {
-  constexpr int NW = 8, NT = 512;
-  constexpr int XV = MV <= 2 ? MV : 0;
+__global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
+  // x rows of MV <= 2 ride in the load ring; more rows are loaded at the start
+  // of the unit, in groups of 4.
+  constexpr int XQ = MV <= 2 ? MV : 0;
+  constexpr int XG = MV < 4 ? MV : 4;
   __shared__ __align__(16) float lds[kLdsFloats];
   __shared__ int s_last;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, t = wave;
-  const int q = lane >> 5, c = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = logical_wg(blockIdx.x, a.G);
-  const int u0 = chunk_begin(g, a.U, a.G), u1 = chunk_begin(g + 1, a.U, a.G);
-  const int RK = a.RK;
+  const int U = a.U, RK = a.RK, S = a.S;
+  const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
   uint32_t* patch = reinterpret_cast<uint32_t*>(lds) + wave * 1024;
 
-  float acc[MV];
+  float acc[2][MV];
 #pragma unroll
-  for (int m = 0; m < MV; ++m) acc[m] = 0.f;
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
-  uint32_t off[1][4];
-  int wbase = u0;
-  load_offsets<1, NW>(a, wbase, u1, wave, lane, off);
+  const uint32_t tile_bytes = (uint32_t)RK * kRecBytes;
+  const uint32_t eo_bytes = (uint32_t)((a.w.nb + 1) * 4);
+  const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0
+  const rsrc_t r_et = make_rsrc(a.w.e_top, (uint32_t)a.N);
+  const rsrc_t r_x = make_rsrc(a.x, x_bytes);
+  const uint32_t v_hi = wave * 1024 + lane * 16;
+  const uint32_t v_lo = kHiBytes + wave * 512 + lane * 8;
+  const uint32_t v_et = (uint32_t)(lane & 28);
+  // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
+  const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
 
-  int nl = u0, lp = u0 / RK, lr = u0 - (u0 / RK) * RK;
-  auto load_next = [&](StageV<XV>& st) __attribute__((always_inline)) {
-    if (nl < u1) {
-      if (nl - wbase >= 64) {
-        wbase = nl;
-        load_offsets<1, NW>(a, wbase, u1, wave, lane, off);
-      }
-      const int li = nl - wbase;
-      const bool mine = 2 * lp + q < a.S;
-      const uint8_t* rb = a.w.rec + ((int64_t)(2 * lp + q) * RK + lr) * kRecBytes;
+  auto issue_off = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
+    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
+    const u32x2 o0 = bload2(r, 0, b0 * 4);
+    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
+    s.off[0][0] = o0.x;
+    s.off[0][1] = o0.y;
+    s.off[1][0] = o1.x;
+    s.off[1][1] = o1.y;
+  };
+  auto issue_w = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const bool live = it.u < u1;
+    const bool has1 = 2 * it.p + 1 < S;
+    const uint32_t bytes = live ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
+    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * it.p) * tile_bytes, bytes);
+    const uint32_t so = (uint32_t)it.r * kRecBytes;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (mine) {
-          st.hi[h] = stream_load<u32x4>(rb + t * 1024 + (c + 32 * h) * 16);
-          st.lo[h] = stream_load<u32x2>(rb + kHiBytes + t * 512 + (c + 32 * h) * 8);
-        } else {
-          st.hi[h] = u32x4{0, 0, 0, 0};
-          st.lo[h] = u32x2{0, 0};
-        }
-      }
-      const uint32_t o0 = __builtin_amdgcn_readlane(off[0][0], li);
-      const uint32_t e0 = __builtin_amdgcn_readlane(off[0][1], li);
-      const uint32_t o1 = __builtin_amdgcn_readlane(off[0][2], li);
-      const uint32_t e1 = __builtin_amdgcn_readlane(off[0][3], li);
-      st.cnt[0] = (int)(e0 - o0);
-      st.cnt[1] = (int)(e1 - o1);
-      st.eb[0] = o0;
-      st.eb[1] = o1;
-      st.e[0] = lane < (int)(e0 - o0) ? a.w.esc[o0 + lane] : 0u;
-      st.e[1] = lane < (int)(e1 - o1) ? a.w.esc[o1 + lane] : 0u;
-      st.bias = mine ? bias2_of(a.w.e_top[lp * 64 + lane]) : 0u;
-      if constexpr (XV > 0) {
+    for (int q = 0; q < 2; ++q) {
+      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
+      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
+    }
+    s.et[0] = bload1(r_et, v_et, (uint32_t)it.p * 64);
+    s.et[1] = bload1(r_et, v_et, (uint32_t)it.p * 64 + 32);
+    if constexpr (XQ > 0) {
+      const rsrc_t rx = make_rsrc(a.x, live ? x_bytes : 0u);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int m = 0; m < XV; ++m) {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(
-                a.x + (int64_t)m * a.K + lr * kRecK + t * kSubK + 16 * h);
-            st.xv[h][m][0] = xp[0];
-            st.xv[h][m][1] = xp[1];
-          }
+      for (int m = 0; m < XQ; ++m) {
+        const uint32_t so_x = m * row_bytes + (uint32_t)it.r * 512;
+        s.xv[m][0] = bload4(rx, v_x, so_x);
+        s.xv[m][1] = bload4(rx, v_x + 16, so_x);
       }
     }
-    ++nl;
-    if (++lr == RK) { lr = 0; ++lp; }
+  };
+  auto issue_e = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
+    const bool has1 = 2 * it.p + 1 < S;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = s.off[q][0];
+      const int c = (q == 0 || has1) ? (int)(s.off[q][1] - o) : 0;
+      s.e[q] = a.w.esc[c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u];
+    }
   };
 
+  // ---- tile end: fold the two k halves, reduce the 8 waves, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
     const bool whole = p * RK >= u0 && (p + 1) * RK <= u1;
-    const int slot = partial_slot(g, p, a.U, a.G, RK);
-    __syncthreads();
+    const int slot = partial_slot(g, p, U, a.G, RK);
+    lds_barrier();
 #pragma unroll
-    for (int m = 0; m < MV; ++m) lds[(wave * MV + m) * 64 + lane] = acc[m];
-    __syncthreads();
-    for (int e = tid; e < MV * 16; e += NT) {
-      const int m = e >> 4, c4 = (e & 15) * 4;
-      float4 v = *reinterpret_cast<const float4*>(lds + m * 64 + c4);
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int w = 1; w < NW; ++w)
-        v = f4add(v, *reinterpret_cast<const float4*>(lds + (w * MV + m) * 64 + c4));
+      for (int m = 0; m < MV; ++m) {
+        const float v = acc[q][m] + __shfl_xor(acc[q][m], 32, 64);
+        if (lane < 32) lds[((wave * 2 + q) * MV + m) * 32 + lane] = v;
+      }
+    lds_barrier();
+    for (int e = tid; e < MV * 16; e += kNT) {
+      const int m = e >> 4, c4 = (e & 15) * 4, q = c4 >> 5, c = c4 & 31;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kNW; ++w)
+        v = f4add(v, *reinterpret_cast<const float4*>(lds + ((w * 2 + q) * MV + m) * 32 + c));
       if (whole) {
         emit4<EPI>(a, tid, m, p * 64 + c4, v);
-      } else {
-        *reinterpret_cast<float4*>(a.part + ((int64_t)slot * a.M + m) * 64 + c4) = v;
+      } else if (m < a.M) {
+          store_partial(a, slot, m, c4, v);
       }
     }
-    __syncthreads();
-    if (!whole) finish_split_tile<EPI>(a, p, tid, NT, &s_last);
+    lds_barrier();
+    if (!whole) finish_split_tile<EPI>(a, p, tid, &s_last);
 #pragma unroll
-    for (int m = 0; m < MV; ++m) acc[m] = 0.f;
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
+  };
+
+  auto dot16 = [&](const uint32_t (&P)[8], u32x4 x0, u32x4 x1, float sum) __attribute__((always_inline)) {
+    const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, P[i]),
+                                            __builtin_bit_cast(bf16x2, xs[i]), sum, false);
+    return sum;
   };
 
   int cp = u0 / RK, cr = u0 - (u0 / RK) * RK, tile = cp;
-  auto step = [&](const StageV<XV>& st) __attribute__((always_inline)) {
+  auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
     if (cp != tile) {
       flush(tile);
       tile = cp;
     }
+    const bool has1 = 2 * cp + 1 < S;
+    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
+    const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
     uint32_t P[2][8];
+    decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y},
+             bias2_of(etop_byte(s.et[0], lane)), P[0]);
+    decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y},
+             bias2_of(etop_byte(s.et[1], lane)), P[1]);
+    if (cnt0 + cnt1 > 0) {
+      patch_store(patch, lane, P[0]);
+      patch_store(patch + 512, lane, P[1]);
+      wave_lds_order();
+      const int cq[2] = {cnt0, cnt1};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      decode16(uint4{st.hi[h].x, st.hi[h].y, st.hi[h].z, st.hi[h].w},
-               uint2{st.lo[h].x, st.lo[h].y}, st.bias, P[h]);
-    if (st.cnt[0] + st.cnt[1] > 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *reinterpret_cast<uint4*>(patch + h * 512 + lane * 8) = make_uint4(P[h][0], P[h][1], P[h][2], P[h][3]);
-        *reinterpret_cast<uint4*>(patch + h * 512 + lane * 8 + 4) = make_uint4(P[h][4], P[h][5], P[h][6], P[h][7]);
+      for (int q = 0; q < 2; ++q) {
+        if (lane < cq[q]) patch_put(patch + q * 512, s.e[q]);
+        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 512, a.w.esc[s.off[q][0] + j]);
       }
-      wave_lds_sync();
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        auto put = [&](uint32_t e) __attribute__((always_inline)) {
-          const uint32_t kk = esc_kk(e);
-          reinterpret_cast<uint16_t*>(patch + (kk >> 4) * 512 + (32 * qq + esc_c(e)) * 8)[kk & 15u] =
-              esc_bits(e);
-        };
-        if (lane < st.cnt[qq]) put(st.e[qq]);
-        for (int j = 64 + lane; j < st.cnt[qq]; j += 64) put(a.w.esc[st.eb[qq] + j]);
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 r0 = *reinterpret_cast<const uint4*>(patch + h * 512 + lane * 8);
-        const uint4 r1 = *reinterpret_cast<const uint4*>(patch + h * 512 + lane * 8 + 4);
-        P[h][0] = r0.x; P[h][1] = r0.y; P[h][2] = r0.z; P[h][3] = r0.w;
-        P[h][4] = r1.x; P[h][5] = r1.y; P[h][6] = r1.z; P[h][7] = r1.w;
-      }
+      wave_lds_order();
+      patch_load(patch, lane, P[0]);
+      patch_load(patch + 512, lane, P[1]);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    if constexpr (XQ > 0) {
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
-        u32x4 x0, x1;
-        if constexpr (XV > 0) {
-          x0 = st.xv[h][m < XV ? m : 0][0];
-          x1 = st.xv[h][m < XV ? m : 0][1];
-        } else {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(
-              a.x + (int64_t)m * a.K + cr * kRecK + t * kSubK + 16 * h);
-          x0 = xp[0];
-          x1 = xp[1];
-        }
-        const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        float s = acc[m];
+        acc[0][m] = dot16(P[0], s.xv[m][0], s.xv[m][1], acc[0][m]);
+        acc[1][m] = dot16(P[1], s.xv[m][0], s.xv[m][1], acc[1][m]);
+      }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, P[h][i]),
-                                              __builtin_bit_cast(bf16x2, xs[i]), s, false);
-        acc[m] = s;
+      for (int m0 = 0; m0 < MV; m0 += XG) {
+        u32x4 xl[XG][2];
+#pragma unroll
+        for (int i = 0; i < XG; ++i) {
+          const uint32_t so_x = (m0 + i) * row_bytes + (uint32_t)cr * 512;
+          xl[i][0] = bload4(r_x, v_x, so_x);
+          xl[i][1] = bload4(r_x, v_x + 16, so_x);
+        }
+#pragma unroll
+        for (int i = 0; i < XG; ++i) {
+          acc[0][m0 + i] = dot16(P[0], xl[i][0], xl[i][1], acc[0][m0 + i]);
+          acc[1][m0 + i] = dot16(P[1], xl[i][0], xl[i][1], acc[1][m0 + i]);
+        }
       }
     }
-    if (++cr == RK) { cr = 0; ++cp; }
+    if (++cr == RK) {
+      cr = 0;
+      ++cp;
+    }
   };
 
   if (u0 < u1) {
-    StageV<XV> sA, sB, sC;
-    load_next(sA);
-    load_next(sB);
-    for (int u = u0; u < u1; u += 3) {
-      load_next(sC);
-      step(sA);
-      if (u + 1 >= u1) break;
-      load_next(sA);
-      step(sB);
-      if (u + 2 >= u1) break;
-      load_next(sB);
-      step(sC);
-    }
+    Ring<XQ> ring;
+    constexpr int NS = Ring<XQ>::NS;
+    UnitIt itO, itW;
+    itO.init(u0, RK);
+    itW.init(u0, RK);
+    issue_off(ring.s[0], itO);
+    itO.next(RK);
+    static_for<kDepth>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      issue_off(ring.s[j + 1], itO);
+      itO.next(RK);
+      issue_w(ring.s[j], itW);
+      issue_e(ring.s[j], itW);
+      itW.next(RK);
+    });
+    auto iteration = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      issue_off(ring.s[(k + kDepth + 1) % NS], itO);
+      itO.next(RK);
+      issue_w(ring.s[(k + kDepth) % NS], itW);
+      issue_e(ring.s[(k + kDepth) % NS], itW);
+      itW.next(RK);
+      step(ring.s[k]);
+    };
+    // Steady state without conditional steps: a skipped step inside the
+    // unrolled body would make the compiler's load-wait counts assume fewer
+    // loads in flight and wait for the next units' loads as well.
+    int base = u0;
+    for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
+    static_for<NS>([&](auto kc) {
+      if (base + decltype(kc)::value < u1) iteration(kc);
+    });
     flush(tile);
   }
-  finish_grid<EPI>(a, tid, NT, &s_last);
+  finish_grid<EPI>(a, tid, &s_last);
+}
+
+// ============================================================================ x rearrangement
+
+// x [M, K] bf16 row-major -> MFMA B fragments. Chunk (b, mt, i, l) of 16 bytes
+// holds x[mt*32 + l%32][32 b + 16 (l/32) + 8 i .. +7] at byte
+// ((b * MT + mt) * 2 + i) * 1024 + l * 16; rows >= M are zero.
+__global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                    int MT, uint4* __restrict__ xf) {
+  const int64_t total = (int64_t)(K / 32) * MT * 128;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total; c += (int64_t)gridDim.x * 256) {
+    const int l = (int)(c & 63), i = (int)((c >> 6) & 1);
+    const int64_t bm = c >> 7;
+    const int mt = (int)(bm % MT), b = (int)(bm / MT);
+    const int m = mt * 32 + (l & 31);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + b * 32 + 16 * (l >> 5) + 8 * i);
+    xf[c] = v;
+  }
 }
 
 // ============================================================================ dispatch
 
-template <int EPI>
-hipError_t launch_mfma(const GemmParams& p, hipStream_t s) {
-  const int mt = (p.M + 31) / 32;
-  dim3 grid(p.G);
-#define W12_MFMA(MT, NW)                                                                     \
-  case MT:                                                                                   \
-    hipLaunchKernelGGL((gemm_mfma_kernel<MT, NW, EPI>), grid, dim3(NW * 64), 0, s, p); \
-    break;
-  switch (mt) {
-    W12_MFMA(1, 8)
-    W12_MFMA(2, 8)
-    W12_MFMA(3, 8)
-    W12_MFMA(4, 8)
-    W12_MFMA(5, 4)
-    W12_MFMA(6, 4)
-    W12_MFMA(7, 4)
-    W12_MFMA(8, 4)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef W12_MFMA
-  return hipGetLastError();
-}
+struct KernelSel {
+  const void* fn;
+  int mt;  // 32-row tiles of the MFMA path (0: VALU path)
+};
 
 template <int EPI>
-hipError_t launch_valu(const GemmParams& p, hipStream_t s) {
-  dim3 grid(p.G);
+KernelSel select_kernel(int M) {
+  if (M >= 16) {
+    switch ((M + 31) / 32) {
+#define W12_MFMA(MT) \
+  case MT:           \
+    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<MT, EPI>), MT};
+      W12_MFMA(1) W12_MFMA(2) W12_MFMA(3) W12_MFMA(4)
+      W12_MFMA(5) W12_MFMA(6) W12_MFMA(7) W12_MFMA(8)
+#undef W12_MFMA
+      default:
+        return {nullptr, 0};
+    }
+  }
+  const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  switch (mv) {
 #define W12_VALU(MV) \
   case MV:           \
-    hipLaunchKernelGGL((gemm_valu_kernel<MV, EPI>), grid, dim3(512), 0, s, p); \
-    break;
-  switch (p.M) {
-    W12_VALU(1) W12_VALU(2) W12_VALU(3) W12_VALU(4) W12_VALU(5)
-    W12_VALU(6) W12_VALU(7) W12_VALU(8) W12_VALU(9) W12_VALU(10)
-    W12_VALU(11) W12_VALU(12) W12_VALU(13) W12_VALU(14) W12_VALU(15)
-    default:
-      return hipErrorInvalidValue;
-  }
+    return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI>), 0};
+    W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(16)
 #undef W12_VALU
-  return hipGetLastError();
+    default:
+      return {nullptr, 0};
+  }
 }
 
 }  // namespace
 
-constexpr int kMfmaMinRows = 16;
-constexpr size_t kCounterBytes = size_t(4) << 18;            // u32 per tile, P <= 2^18
-constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + keys + done, aligned
+constexpr size_t kCounterBytes = size_t(4) << 18;              // u32 per tile, P <= 2^18
+constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + argmax keys + done counter
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
   const int64_t S = n / kStrip, P = (S + 1) / 2, RK = k / kRecK, U = P * RK;
-  const int per_cu = 2;
-  int64_t G = (int64_t)num_cu * per_cu;
+  // one 8-wave workgroup per compute unit, every slice resident at once
+  int64_t G = num_cu;
   if (G > U) G = U;
   if (G < 1) G = 1;
   pl.G = (int)G;
-  // The counter region has the same place and size for every shape: any
-  // shape's tile counters (P <= 2^18 because N*K < 2^32 and K >= 256), the
-  // argmax keys (m <= 256) and the done counter. Partial sums always start
-  // after it, so a workspace shared by calls of different shapes never has
-  // old partial sums where a later call expects zeroed counters.
-  (void)P;
+  // The counter region has the same place and size for every shape (any
+  // shape's tile counters, the argmax keys and the done counter), so a
+  // workspace shared by calls of different shapes never holds old partial
+  // sums where a later call expects zeroed counters.
   pl.off_cnt = 0;
   pl.off_keys = kCounterBytes;
   pl.off_done = kCounterBytes + 256 * 8;
   pl.off_part = kStateBytes;
-  pl.ws_bytes = kStateBytes + (size_t)2 * G * m * 64 * 4;
+  const size_t part_bytes = (size_t)2 * G * m * 64 * 4;
+  pl.off_xf = (pl.off_part + part_bytes + 255) & ~size_t(255);
+  const int64_t mt = m >= 16 ? (m + 31) / 32 : 0;
+  pl.ws_bytes = pl.off_xf + (size_t)mt * 32 * k * 2;
   return pl;
 }
 
 hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s) {
-  if (p.M >= kMfmaMinRows)
-    return epi == kEpiY ? launch_mfma<kEpiY>(p, s) : launch_mfma<kEpiArgmax>(p, s);
-  return epi == kEpiY ? launch_valu<kEpiY>(p, s) : launch_valu<kEpiArgmax>(p, s);
+  const KernelSel k = epi == kEpiY ? select_kernel<kEpiY>(p.M) : select_kernel<kEpiArgmax>(p.M);
+  if (!k.fn) return hipErrorInvalidValue;
+  if (k.mt > 0) {
+    const int64_t chunks = (int64_t)(p.K / 32) * k.mt * 128;
+    const int64_t want = (chunks + 255) / 256;
+    const int blocks = (int)(want < 2048 ? want : 2048);
+    hipLaunchKernelGGL(xfrag_kernel, dim3(blocks), dim3(256), 0, s, p.x, p.M, p.K, k.mt, p.xf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  return hipLaunchKernel(k.fn, dim3(p.G), dim3(kNT), args, 0, s);
 }
 
 }  // namespace w12

@@ -30,6 +30,7 @@ struct GemmParams {
   int G;   // workgroups
   void* y;
   int ytype;
+  uint4* xf;              // x rearranged into MFMA B fragments (m >= 16)
   float* part;            // [2G][M][64] split-tile partial sums
   uint32_t* tile_cnt;     // [P] arrival counters, zero between calls
   unsigned long long* keys;  // [M] argmax keys, zero between calls
@@ -41,7 +42,7 @@ struct GemmParams {
 struct GemmPlan {
   int G;
   size_t ws_bytes;
-  size_t off_cnt, off_part, off_keys, off_done;
+  size_t off_cnt, off_part, off_keys, off_done, off_xf;
 };
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu);
