@@ -196,9 +196,9 @@ __device__ __forceinline__ void writes_done_barrier() {
 }
 
 // Last contributor of a split tile sums the partials in slice order.
+// Called after writes_done_barrier(), once per split tile of the slice.
 template <int EPI>
 __device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_last) {
-  writes_done_barrier();
   const int gf = owner_of(p * a.RK, a.U, a.G);
   const int gl = owner_of((p + 1) * a.RK - 1, a.U, a.G);
   if (tid == 0) {
@@ -238,6 +238,26 @@ __device__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
       if (tid == 0) atomicExch(a.done, 0u);
     }
   }
+}
+
+// A tile is split when the slice [u0, u1) does not hold all of its units.
+__device__ __forceinline__ bool tile_is_split(int p, int u0, int u1, int RK) {
+  return !(p * RK >= u0 && (p + 1) * RK <= u1);
+}
+
+// End of a workgroup's slice. The partial sums of the (at most two) tiles it
+// shares with its neighbours were stored when those tiles ended; the hand-off
+// waits until now, so no memory round trip stalled the stream. Then, for the
+// argmax epilogue, the grid-wide key-to-id step.
+template <int EPI>
+__device__ void finish_slice(const GemmParams& a, int tid, int u0, int u1, int* s_last) {
+  const int RK = a.RK, p0 = u0 / RK, p1 = (u1 - 1) / RK;
+  const bool s0 = u0 < u1 && tile_is_split(p0, u0, u1, RK);
+  const bool s1 = u0 < u1 && p1 != p0 && tile_is_split(p1, u0, u1, RK);
+  if (s0 || s1 || EPI == kEpiArgmax) writes_done_barrier();
+  if (s0) finish_split_tile<EPI>(a, p0, tid, s_last);
+  if (s1) finish_split_tile<EPI>(a, p1, tid, s_last);
+  finish_grid<EPI>(a, tid, s_last);
 }
 
 // Window top of this lane's channel from the dword holding it (channel index
@@ -426,7 +446,6 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       }
     });
     lds_barrier();
-    if (!whole) finish_split_tile<EPI>(a, p, tid, &s_last);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -533,7 +552,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     });
     flush(tile);
   }
-  finish_grid<EPI>(a, tid, &s_last);
+  finish_slice<EPI>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ VALU path (m < 16)
@@ -641,7 +660,6 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       }
     }
     lds_barrier();
-    if (!whole) finish_split_tile<EPI>(a, p, tid, &s_last);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -749,7 +767,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     });
     flush(tile);
   }
-  finish_grid<EPI>(a, tid, &s_last);
+  finish_slice<EPI>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ x rearrangement
