@@ -75,7 +75,7 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
   p.RK = (int)(w->k / 256);
   p.S = (int)(w->n / 32);
   p.P = (p.S + 1) / 2;
-  p.U = p.P * p.RK;
+  p.U = pl.U;
   p.G = pl.G;
   p.y = y;
   p.ytype = ytype;

@@ -123,10 +123,8 @@ __device__ __forceinline__ int chunk_begin(int g, int U, int G) {
 __device__ __forceinline__ int owner_of(int u, int U, int G) {
   return (int)(((int64_t)(u + 1) * G + U - 1) / U) - 1;
 }
-// Partial-sum slot of workgroup g for tile p: its first tile or its last.
-__device__ __forceinline__ int partial_slot(int g, int p, int U, int G, int RK) {
-  return (p == chunk_begin(g, U, G) / RK) ? 2 * g : 2 * g + 1;
-}
+
+__device__ __forceinline__ unsigned long long row16_max(unsigned long long v);
 
 // Final value of 4 consecutive channels (n .. n+3) of row m. For the argmax
 // epilogue, 16 consecutive threads of a wave hold one row's 64 channels.
@@ -155,13 +153,7 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
         best = key > best ? key : best;
       }
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
-      const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
-      const unsigned long long w = ((unsigned long long)hi << 32) | lo;
-      best = w > best ? w : best;
-    }
+    best = row16_max(best);
     if ((tid & 15) == 0 && best) atomicMax(&a.keys[m], best);
   }
 }
@@ -176,14 +168,20 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
 // with device-scope loads that bypass its L2, so it cannot see stale lines.
 constexpr int kDeviceScope = 16;  // sc1 cache-policy bit: coherent across XCDs
 
+// Partial sums: slot (2g or 2g+1: the workgroup's first or last tile) x row
+// x 64 channels.
+__device__ __forceinline__ uint32_t partial_off(const GemmParams& a, int slot, int m, int c4) {
+  return (uint32_t)(((slot * a.M + m) * 64 + c4) * 4);
+}
+__device__ __forceinline__ rsrc_t partial_rsrc(const GemmParams& a) {
+  return make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
+}
 __device__ __forceinline__ void store_partial(const GemmParams& a, int slot, int m, int c4, float4 v) {
-  const rsrc_t r = make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
   const u32x4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(d, r, (uint32_t)((slot * a.M + m) * 64 + c4) * 4u, 0, kDeviceScope);
+  __builtin_amdgcn_raw_buffer_store_b128(d, partial_rsrc(a), partial_off(a, slot, m, c4), 0, kDeviceScope);
 }
 __device__ __forceinline__ float4 load_partial(const GemmParams& a, int slot, int m, int c4) {
-  const rsrc_t r = make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
-  const u32x4 d = bload4<kDeviceScope>(r, (uint32_t)((slot * a.M + m) * 64 + c4) * 4u, 0);
+  const u32x4 d = bload4<kDeviceScope>(partial_rsrc(a), partial_off(a, slot, m, c4), 0);
   return make_float4(__uint_as_float(d.x), __uint_as_float(d.y), __uint_as_float(d.z), __uint_as_float(d.w));
 }
 // Every thread's earlier global writes and atomics are acknowledged, then
@@ -195,8 +193,17 @@ __device__ __forceinline__ void writes_done_barrier() {
   __syncthreads();
 }
 
-// Last contributor of a split tile sums the partials in slice order.
-// Called after writes_done_barrier(), once per split tile of the slice.
+// A tile is split when the slice [u0, u1) does not hold all of its units.
+__device__ __forceinline__ bool tile_is_split(int p, int u0, int u1, int RK) {
+  return !(p * RK >= u0 && (p + 1) * RK <= u1);
+}
+// Partial-sum slot of workgroup g for tile p: its first tile or its last.
+__device__ __forceinline__ int partial_slot(int g, int p, int U, int G, int RK) {
+  return (p == chunk_begin(g, U, G) / RK) ? 2 * g : 2 * g + 1;
+}
+
+// Last contributor of a split tile sums the partials in slice order. Called
+// after writes_done_barrier(), once per split tile of the slice.
 template <int EPI>
 __device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_last) {
   const int gf = owner_of(p * a.RK, a.U, a.G);
@@ -240,11 +247,6 @@ __device__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
   }
 }
 
-// A tile is split when the slice [u0, u1) does not hold all of its units.
-__device__ __forceinline__ bool tile_is_split(int p, int u0, int u1, int RK) {
-  return !(p * RK >= u0 && (p + 1) * RK <= u1);
-}
-
 // End of a workgroup's slice. The partial sums of the (at most two) tiles it
 // shares with its neighbours were stored when those tiles ended; the hand-off
 // waits until now, so no memory round trip stalled the stream. Then, for the
@@ -260,32 +262,88 @@ __device__ void finish_slice(const GemmParams& a, int tid, int u0, int u1, int* 
   finish_grid<EPI>(a, tid, s_last);
 }
 
-// Window top of this lane's channel from the dword holding it (channel index
-// = 4j + (lane & 3) within every strip).
-__device__ __forceinline__ uint32_t etop_byte(uint32_t dw, int lane) {
-  return (dw >> (8 * (lane & 3))) & 0xFFu;
+// (E_n - 15) << 7 in both 16-bit halves for this lane's channel, from the
+// dword of window tops holding it (channel 4j + (lane & 3) of the strip):
+// one bit-field extract and one 24-bit multiply-add.
+__device__ __forceinline__ uint32_t lane_bias2(uint32_t dw, uint32_t shift) {
+  const uint32_t e = __builtin_amdgcn_ubfe(dw, shift, 8);
+  return e * 0x00800080u - 0x07800780u;
 }
 
-// Per-wave patch buffer of one strip: 2 KB = [k half j/8][lane][4 dwords], so
-// each 16-byte LDS access of the wave covers consecutive addresses.
-__device__ __forceinline__ void patch_store(uint32_t* buf, int lane, const uint32_t (&p)[8]) {
-  *reinterpret_cast<uint4*>(buf + lane * 4) = make_uint4(p[0], p[1], p[2], p[3]);
-  *reinterpret_cast<uint4*>(buf + 256 + lane * 4) = make_uint4(p[4], p[5], p[6], p[7]);
+// Per-wave patch buffer of one strip: 2 KB of restored weights laid out as
+// halfword k4 * 512 + k3 * 256 + c * 8 + (kk & 7) for weight (channel c,
+// subtile column kk = 16 k4 + 8 k3 + (kk & 7)). Lane c + 32 h writes its pairs
+// 0..3 at byte h * 1024 + c * 16 and 4..7 at 512 bytes further on, so each
+// half-wave of a 16-byte access covers 512 consecutive bytes.
+__device__ __forceinline__ uint32_t patch_lane_off(int lane) {
+  return (uint32_t)(lane & 31) * 16u + (uint32_t)(lane >> 5) * 1024u;
 }
-__device__ __forceinline__ void patch_load(const uint32_t* buf, int lane, uint32_t (&p)[8]) {
-  const uint4 r0 = *reinterpret_cast<const uint4*>(buf + lane * 4);
-  const uint4 r1 = *reinterpret_cast<const uint4*>(buf + 256 + lane * 4);
+__device__ __forceinline__ void patch_store(char* buf, uint32_t lo, const uint32_t (&p)[8]) {
+  *reinterpret_cast<uint4*>(buf + lo) = make_uint4(p[0], p[1], p[2], p[3]);
+  *reinterpret_cast<uint4*>(buf + lo + 512) = make_uint4(p[4], p[5], p[6], p[7]);
+}
+__device__ __forceinline__ void patch_load(const char* buf, uint32_t lo, uint32_t (&p)[8]) {
+  const uint4 r0 = *reinterpret_cast<const uint4*>(buf + lo);
+  const uint4 r1 = *reinterpret_cast<const uint4*>(buf + lo + 512);
   p[0] = r0.x; p[1] = r0.y; p[2] = r0.z; p[3] = r0.w;
   p[4] = r1.x; p[5] = r1.y; p[6] = r1.z; p[7] = r1.w;
 }
-// Overwrite one restored weight with an escape entry (bits << 16 | c << 5 |
-// kk): it sits at position kk % 16 of lane c + 32 (kk / 16).
-__device__ __forceinline__ void patch_put(uint32_t* buf, uint32_t e) {
-  const uint32_t kk = esc_kk(e), owner = esc_c(e) + ((kk >> 4) << 5), j = kk & 15u;
-  reinterpret_cast<uint16_t*>(buf + (j >> 3) * 256 + owner * 4)[j & 7u] = esc_bits(e);
+// Overwrite one restored weight with an escape entry (bits << 16 | c << 5 | kk):
+// its byte in the layout above, straight from the entry's low bits.
+__device__ __forceinline__ void patch_put(char* buf, uint32_t e) {
+  const uint32_t at = ((e << 6) & 0x600u) | ((e >> 1) & 0x1F0u) | ((e << 1) & 0xEu);
+  *reinterpret_cast<uint16_t*>(buf + at) = esc_bits(e);
 }
 
-// Position in a workgroup's slice of units.
+// Restore the lane's 2 x 16 weights of a unit (both strips of the tile) and
+// apply the escape blocks' entries: the restored pairs go to the wave's LDS
+// patch buffer, the lanes holding entries overwrite their slots, the pairs are
+// read back. Only the wave itself touches its buffer.
+template <typename SlotT>
+__device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uint32_t bias1, bool has0,
+                                             bool has1, char* patch, uint32_t plo, int lane, rsrc_t r_esc,
+                                             uint32_t (&P)[2][8]) {
+  const int cnt0 = has0 ? __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0])) : 0;
+  const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
+  decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y}, bias0, P[0]);
+  decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y}, bias1, P[1]);
+  if (cnt0 + cnt1 > 0) {
+    patch_store(patch, plo, P[0]);
+    patch_store(patch + 2048, plo, P[1]);
+    wave_lds_order();
+    const int cq[2] = {cnt0, cnt1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
+      if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
+        const uint32_t o = __builtin_amdgcn_readfirstlane(s.off[q][0]);
+        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
+      }
+    }
+    wave_lds_order();
+    patch_load(patch, plo, P[0]);
+    patch_load(patch + 2048, plo, P[1]);
+  }
+}
+
+// Row maximum of (value key, ~index) over the 16 lanes of a DPP row: after
+// exchanges with lane ^ 1, lane ^ 2, the mirrored half-row and the mirrored
+// row, every lane of the row holds the maximum.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long max_dpp(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  const unsigned long long w = ((unsigned long long)hi << 32) | lo;
+  return w > v ? w : v;
+}
+__device__ __forceinline__ unsigned long long row16_max(unsigned long long v) {
+  v = max_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = max_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = max_dpp<0x141>(v);  // row_half_mirror
+  return max_dpp<0x140>(v);  // row_mirror
+}
+
+// Position in a workgroup's slice of units: tile and record.
 struct UnitIt {
   int u, p, r;
   __device__ __forceinline__ void init(int u0, int RK) {
@@ -302,13 +360,13 @@ struct UnitIt {
   }
 };
 
-// One unit's loads for one wave (subtile t = wave of both strips).
+// One unit's loads for one wave (subtile t = wave of both strips of a tile).
 template <int XQ>
 struct Slot {
   uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
   u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[2];         // their low nibbles
-  uint32_t et[2];      // dword holding the lane's channel's window top
+  uint32_t et[2];      // dword holding the lane's channel's window top (tile starts)
   uint32_t e[2];       // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ > 0 ? XQ : 1][2];  // x operands that ride with the unit
 };
@@ -328,6 +386,95 @@ struct Ring {
   Slot<XQ> s[NS];
 };
 
+// The per-unit loads shared by both kernels. Strips past the last (the
+// missing second strip of a final tile) and units past the slice load
+// nothing: their resources are empty.
+template <int XQ>
+struct UnitLoads {
+  const GemmParams& a;
+  int u0, u1, wave, lane, RK, S;
+  uint32_t tile_bytes, eo_bytes, v_hi, v_lo, v_et;
+  rsrc_t r_esc;
+
+  __device__ __forceinline__ void issue_off(Slot<XQ>& s, const UnitIt& it) const {
+    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
+    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
+    const u32x2 o0 = bload2(r, 0, b0 * 4);
+    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
+    s.off[0][0] = o0.x;
+    s.off[0][1] = o0.y;
+    s.off[1][0] = o1.x;
+    s.off[1][1] = o1.y;
+  }
+  __device__ __forceinline__ void issue_w(Slot<XQ>& s, const UnitIt& it) const {
+    const int p = it.p;
+    const bool live = it.u < u1, has0 = 2 * p < S, has1 = 2 * p + 1 < S;
+    const uint32_t bytes = (live && has0) ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
+    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * p) * tile_bytes, bytes);
+    const uint32_t so = (uint32_t)it.r * kRecBytes;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
+      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
+    }
+    // window tops change per tile: fetched at a tile's first record and at
+    // the slice's first unit
+    const bool et_now = live && (it.r == 0 || it.u == u0);
+    const rsrc_t r_et = make_rsrc(a.w.e_top, et_now ? (uint32_t)a.N : 0u);
+    s.et[0] = bload1(r_et, v_et, (uint32_t)p * 64);
+    s.et[1] = bload1(r_et, v_et, (uint32_t)p * 64 + 32);
+  }
+  __device__ __forceinline__ void issue_e(Slot<XQ>& s, const UnitIt& it) const {
+    const int p = it.p;
+    const bool has[2] = {2 * p < S, 2 * p + 1 < S};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = s.off[q][0];
+      const int c = has[q] ? (int)(s.off[q][1] - o) : 0;
+      s.e[q] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u) * 4u, 0);
+    }
+  }
+};
+
+// The slice walk: prologue, steady state without conditional steps (a skipped
+// step inside the unrolled body would make the compiler's load-wait counts
+// assume fewer loads in flight and wait for the next units' loads as well),
+// and a guarded tail of fewer than NS units.
+template <int XQ, typename LoadsT, typename XF, typename StepF>
+__device__ __forceinline__ void walk_slice(const LoadsT& L, int u0, int u1, int RK, XF&& issue_x, StepF&& step) {
+  Ring<XQ> ring;
+  constexpr int NS = Ring<XQ>::NS;
+  UnitIt itO, itW;
+  itO.init(u0, RK);
+  itW.init(u0, RK);
+  L.issue_off(ring.s[0], itO);
+  itO.next(RK);
+  static_for<kDepth>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    L.issue_off(ring.s[j + 1], itO);
+    itO.next(RK);
+    L.issue_w(ring.s[j], itW);
+    issue_x(ring.s[j], itW);
+    L.issue_e(ring.s[j], itW);
+    itW.next(RK);
+  });
+  auto iteration = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    L.issue_off(ring.s[(k + kDepth + 1) % NS], itO);
+    itO.next(RK);
+    L.issue_w(ring.s[(k + kDepth) % NS], itW);
+    issue_x(ring.s[(k + kDepth) % NS], itW);
+    L.issue_e(ring.s[(k + kDepth) % NS], itW);
+    itW.next(RK);
+    step(ring.s[k]);
+  };
+  int base = u0;
+  for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
+  static_for<NS>([&](auto kc) {
+    if (base + decltype(kc)::value < u1) iteration(kc);
+  });
+}
+
 // ============================================================================ MFMA path (m >= 16)
 
 template <int MT, int EPI>
@@ -343,7 +490,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   const int g = logical_wg(blockIdx.x, a.G);
   const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
-  uint32_t* patch = reinterpret_cast<uint32_t*>(lds) + wave * 1024;
+  char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
 
   f32x16 acc[2][MT];
 #pragma unroll
@@ -353,42 +500,21 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  const uint32_t tile_bytes = (uint32_t)RK * kRecBytes;  // one strip's records
-  const uint32_t eo_bytes = (uint32_t)((a.w.nb + 1) * 4);
+  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S,
+                             (uint32_t)RK * kRecBytes, (uint32_t)((a.w.nb + 1) * 4),
+                             (uint32_t)(wave * 1024 + lane * 16),
+                             (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                             make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t xf_bytes = (uint32_t)(MT * 32) * (uint32_t)a.K * 2u;
-  const rsrc_t r_et = make_rsrc(a.w.e_top, (uint32_t)a.N);
   const rsrc_t r_xf = make_rsrc(a.xf, xf_bytes);
-  const uint32_t v_hi = wave * 1024 + lane * 16;
-  const uint32_t v_lo = kHiBytes + wave * 512 + lane * 8;
-  const uint32_t v_et = (uint32_t)(lane & 28);
+  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
+  const uint32_t plo = patch_lane_off(lane);
   const uint32_t v_x = (uint32_t)lane * 16u;
 
-  auto issue_off = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
-    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
-    const u32x2 o0 = bload2(r, 0, b0 * 4);
-    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
-    s.off[0][0] = o0.x;
-    s.off[0][1] = o0.y;
-    s.off[1][0] = o1.x;
-    s.off[1][1] = o1.y;
-  };
-  auto issue_w = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const bool live = it.u < u1;
-    const bool has1 = 2 * it.p + 1 < S;
-    const uint32_t bytes = live ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
-    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * it.p) * tile_bytes, bytes);
-    const uint32_t so = (uint32_t)it.r * kRecBytes;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
-      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
-    }
-    s.et[0] = bload1(r_et, v_et, (uint32_t)it.p * 64);
-    s.et[1] = bload1(r_et, v_et, (uint32_t)it.p * 64 + 32);
+  auto issue_x = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
     if constexpr (XQ > 0) {
+      const rsrc_t rx = make_rsrc(a.xf, it.u < u1 ? xf_bytes : 0u);
       const uint32_t b = (uint32_t)it.r * 8 + wave;
-      const rsrc_t rx = make_rsrc(a.xf, live ? xf_bytes : 0u);
 #pragma unroll
       for (int mt = 0; mt < XQ; ++mt) {
         s.xv[mt][0] = bload4(rx, v_x, ((b * MT + mt) * 2 + 0) * 1024);
@@ -396,19 +522,10 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       }
     }
   };
-  auto issue_e = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const bool has1 = 2 * it.p + 1 < S;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t o = s.off[q][0];
-      const int c = (q == 0 || has1) ? (int)(s.off[q][1] - o) : 0;
-      s.e[q] = a.w.esc[c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u];
-    }
-  };
 
   // ---- tile end: reduce the 8 waves' accumulators, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
-    const bool whole = p * RK >= u0 && (p + 1) * RK <= u1;
+    const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
     static_for<MT>([&](auto mtc) {
       constexpr int mt = decltype(mtc)::value;
@@ -430,19 +547,17 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       lds_barrier();
       if (wave < 4) put(lds + wave * kSlotFloats, true);
       lds_barrier();
-      {
-        const int ml = tid >> 4, c4 = (tid & 15) * 4;  // 32 rows x 16 channel quads = kNT
-        const float* b = lds + ml * kRedStride + c4;
-        const float4 v = f4add(f4add(*reinterpret_cast<const float4*>(b),
-                                     *reinterpret_cast<const float4*>(b + kSlotFloats)),
-                               f4add(*reinterpret_cast<const float4*>(b + 2 * kSlotFloats),
-                                     *reinterpret_cast<const float4*>(b + 3 * kSlotFloats)));
-        const int m = mt * 32 + ml;
-        if (whole) {
-          emit4<EPI>(a, tid, m, p * 64 + c4, v);
-        } else if (m < a.M) {
-          store_partial(a, slot, m, c4, v);
-        }
+      const int ml = tid >> 4, c4 = (tid & 15) * 4;  // 32 rows x 16 channel quads = kNT
+      const float* b = lds + ml * kRedStride + c4;
+      const float4 v = f4add(f4add(*reinterpret_cast<const float4*>(b),
+                                   *reinterpret_cast<const float4*>(b + kSlotFloats)),
+                             f4add(*reinterpret_cast<const float4*>(b + 2 * kSlotFloats),
+                                   *reinterpret_cast<const float4*>(b + 3 * kSlotFloats)));
+      const int m = mt * 32 + ml;
+      if (whole) {
+        emit4<EPI>(a, tid, m, p * 64 + c4, v);
+      } else if (m < a.M) {
+        store_partial(a, slot, m, c4, v);
       }
     });
     lds_barrier();
@@ -455,34 +570,23 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   };
 
   // ---- arithmetic of one unit
-  int cp = u0 / RK, cr = u0 - (u0 / RK) * RK, tile = cp;
+  UnitIt cur;
+  cur.init(u0, RK);
+  int tile_open = cur.p;
+  uint32_t bias[2] = {0u, 0u};
   auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
-    if (cp != tile) {
-      flush(tile);
-      tile = cp;
+    if (cur.p != tile_open) {
+      flush(tile_open);
+      tile_open = cur.p;
     }
-    const bool has1 = 2 * cp + 1 < S;
-    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
-    const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
+    const int p = cur.p;
+    const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
+    if (cur.r == 0 || cur.u == u0) {  // new tile: this slot carries its window tops
+      bias[0] = lane_bias2(s.et[0], et_shift);
+      bias[1] = lane_bias2(s.et[1], et_shift);
+    }
     uint32_t P[2][8];
-    decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y},
-             bias2_of(etop_byte(s.et[0], lane)), P[0]);
-    decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y},
-             bias2_of(etop_byte(s.et[1], lane)), P[1]);
-    if (cnt0 + cnt1 > 0) {
-      patch_store(patch, lane, P[0]);
-      patch_store(patch + 512, lane, P[1]);
-      wave_lds_order();
-      const int cq[2] = {cnt0, cnt1};
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if (lane < cq[q]) patch_put(patch + q * 512, s.e[q]);
-        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 512, a.w.esc[s.off[q][0] + j]);
-      }
-      wave_lds_order();
-      patch_load(patch, lane, P[0]);
-      patch_load(patch + 512, lane, P[1]);
-    }
+    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
     u32x4 xl[MT][2];
     if constexpr (XQ > 0) {
 #pragma unroll
@@ -491,7 +595,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
         xl[mt][1] = s.xv[mt][1];
       }
     } else {
-      const uint32_t b = (uint32_t)cr * 8 + wave;
+      const uint32_t b = (uint32_t)cur.r * 8 + wave;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         xl[mt][0] = bload4(r_xf, v_x, ((b * MT + mt) * 2 + 0) * 1024);
@@ -511,46 +615,12 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, b0, acc[1][mt], 0, 0, 0);
       acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, b1, acc[1][mt], 0, 0, 0);
     }
-    if (++cr == RK) {
-      cr = 0;
-      ++cp;
-    }
+    cur.next(RK);
   };
 
   if (u0 < u1) {
-    Ring<XQ> ring;
-    constexpr int NS = Ring<XQ>::NS;
-    UnitIt itO, itW;
-    itO.init(u0, RK);
-    itW.init(u0, RK);
-    issue_off(ring.s[0], itO);
-    itO.next(RK);
-    static_for<kDepth>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      issue_off(ring.s[j + 1], itO);
-      itO.next(RK);
-      issue_w(ring.s[j], itW);
-      issue_e(ring.s[j], itW);
-      itW.next(RK);
-    });
-    auto iteration = [&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      issue_off(ring.s[(k + kDepth + 1) % NS], itO);
-      itO.next(RK);
-      issue_w(ring.s[(k + kDepth) % NS], itW);
-      issue_e(ring.s[(k + kDepth) % NS], itW);
-      itW.next(RK);
-      step(ring.s[k]);
-    };
-    // Steady state without conditional steps: a skipped step inside the
-    // unrolled body would make the compiler's load-wait counts assume fewer
-    // loads in flight and wait for the next units' loads as well.
-    int base = u0;
-    for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
-    static_for<NS>([&](auto kc) {
-      if (base + decltype(kc)::value < u1) iteration(kc);
-    });
-    flush(tile);
+    walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
+    flush(tile_open);
   }
   finish_slice<EPI>(a, tid, u0, u1, &s_last);
 }
@@ -571,7 +641,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   const int g = logical_wg(blockIdx.x, a.G);
   const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
-  uint32_t* patch = reinterpret_cast<uint32_t*>(lds) + wave * 1024;
+  char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
 
   float acc[2][MV];
 #pragma unroll
@@ -579,43 +649,22 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
-  const uint32_t tile_bytes = (uint32_t)RK * kRecBytes;
-  const uint32_t eo_bytes = (uint32_t)((a.w.nb + 1) * 4);
+  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S,
+                             (uint32_t)RK * kRecBytes, (uint32_t)((a.w.nb + 1) * 4),
+                             (uint32_t)(wave * 1024 + lane * 16),
+                             (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                             make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0
-  const rsrc_t r_et = make_rsrc(a.w.e_top, (uint32_t)a.N);
   const rsrc_t r_x = make_rsrc(a.x, x_bytes);
-  const uint32_t v_hi = wave * 1024 + lane * 16;
-  const uint32_t v_lo = kHiBytes + wave * 512 + lane * 8;
-  const uint32_t v_et = (uint32_t)(lane & 28);
+  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
+  const uint32_t plo = patch_lane_off(lane);
   // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
   const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
 
-  auto issue_off = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
-    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
-    const u32x2 o0 = bload2(r, 0, b0 * 4);
-    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
-    s.off[0][0] = o0.x;
-    s.off[0][1] = o0.y;
-    s.off[1][0] = o1.x;
-    s.off[1][1] = o1.y;
-  };
-  auto issue_w = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const bool live = it.u < u1;
-    const bool has1 = 2 * it.p + 1 < S;
-    const uint32_t bytes = live ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
-    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * it.p) * tile_bytes, bytes);
-    const uint32_t so = (uint32_t)it.r * kRecBytes;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
-      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
-    }
-    s.et[0] = bload1(r_et, v_et, (uint32_t)it.p * 64);
-    s.et[1] = bload1(r_et, v_et, (uint32_t)it.p * 64 + 32);
+  auto issue_x = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
     if constexpr (XQ > 0) {
-      const rsrc_t rx = make_rsrc(a.x, live ? x_bytes : 0u);
+      const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
 #pragma unroll
       for (int m = 0; m < XQ; ++m) {
         const uint32_t so_x = m * row_bytes + (uint32_t)it.r * 512;
@@ -624,19 +673,10 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       }
     }
   };
-  auto issue_e = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const bool has1 = 2 * it.p + 1 < S;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t o = s.off[q][0];
-      const int c = (q == 0 || has1) ? (int)(s.off[q][1] - o) : 0;
-      s.e[q] = a.w.esc[c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u];
-    }
-  };
 
   // ---- tile end: fold the two k halves, reduce the 8 waves, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
-    const bool whole = p * RK >= u0 && (p + 1) * RK <= u1;
+    const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
     lds_barrier();
 #pragma unroll
@@ -656,7 +696,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       if (whole) {
         emit4<EPI>(a, tid, m, p * 64 + c4, v);
       } else if (m < a.M) {
-          store_partial(a, slot, m, c4, v);
+        store_partial(a, slot, m, c4, v);
       }
     }
     lds_barrier();
@@ -675,34 +715,23 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     return sum;
   };
 
-  int cp = u0 / RK, cr = u0 - (u0 / RK) * RK, tile = cp;
+  UnitIt cur;
+  cur.init(u0, RK);
+  int tile_open = cur.p;
+  uint32_t bias[2] = {0u, 0u};
   auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
-    if (cp != tile) {
-      flush(tile);
-      tile = cp;
+    if (cur.p != tile_open) {
+      flush(tile_open);
+      tile_open = cur.p;
     }
-    const bool has1 = 2 * cp + 1 < S;
-    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
-    const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
+    const int p = cur.p;
+    const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
+    if (cur.r == 0 || cur.u == u0) {  // new tile: this slot carries its window tops
+      bias[0] = lane_bias2(s.et[0], et_shift);
+      bias[1] = lane_bias2(s.et[1], et_shift);
+    }
     uint32_t P[2][8];
-    decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y},
-             bias2_of(etop_byte(s.et[0], lane)), P[0]);
-    decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y},
-             bias2_of(etop_byte(s.et[1], lane)), P[1]);
-    if (cnt0 + cnt1 > 0) {
-      patch_store(patch, lane, P[0]);
-      patch_store(patch + 512, lane, P[1]);
-      wave_lds_order();
-      const int cq[2] = {cnt0, cnt1};
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if (lane < cq[q]) patch_put(patch + q * 512, s.e[q]);
-        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 512, a.w.esc[s.off[q][0] + j]);
-      }
-      wave_lds_order();
-      patch_load(patch, lane, P[0]);
-      patch_load(patch + 512, lane, P[1]);
-    }
+    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
     if constexpr (XQ > 0) {
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
@@ -715,7 +744,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
         u32x4 xl[XG][2];
 #pragma unroll
         for (int i = 0; i < XG; ++i) {
-          const uint32_t so_x = (m0 + i) * row_bytes + (uint32_t)cr * 512;
+          const uint32_t so_x = (m0 + i) * row_bytes + (uint32_t)cur.r * 512;
           xl[i][0] = bload4(r_x, v_x, so_x);
           xl[i][1] = bload4(r_x, v_x + 16, so_x);
         }
@@ -726,46 +755,12 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
         }
       }
     }
-    if (++cr == RK) {
-      cr = 0;
-      ++cp;
-    }
+    cur.next(RK);
   };
 
   if (u0 < u1) {
-    Ring<XQ> ring;
-    constexpr int NS = Ring<XQ>::NS;
-    UnitIt itO, itW;
-    itO.init(u0, RK);
-    itW.init(u0, RK);
-    issue_off(ring.s[0], itO);
-    itO.next(RK);
-    static_for<kDepth>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      issue_off(ring.s[j + 1], itO);
-      itO.next(RK);
-      issue_w(ring.s[j], itW);
-      issue_e(ring.s[j], itW);
-      itW.next(RK);
-    });
-    auto iteration = [&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      issue_off(ring.s[(k + kDepth + 1) % NS], itO);
-      itO.next(RK);
-      issue_w(ring.s[(k + kDepth) % NS], itW);
-      issue_e(ring.s[(k + kDepth) % NS], itW);
-      itW.next(RK);
-      step(ring.s[k]);
-    };
-    // Steady state without conditional steps: a skipped step inside the
-    // unrolled body would make the compiler's load-wait counts assume fewer
-    // loads in flight and wait for the next units' loads as well.
-    int base = u0;
-    for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
-    static_for<NS>([&](auto kc) {
-      if (base + decltype(kc)::value < u1) iteration(kc);
-    });
-    flush(tile);
+    walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
+    flush(tile_open);
   }
   finish_slice<EPI>(a, tid, u0, u1, &s_last);
 }
@@ -777,16 +772,15 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 // ((b * MT + mt) * 2 + i) * 1024 + l * 16; rows >= M are zero.
 __global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                     int MT, uint4* __restrict__ xf) {
-  const int64_t total = (int64_t)(K / 32) * MT * 128;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total; c += (int64_t)gridDim.x * 256) {
-    const int l = (int)(c & 63), i = (int)((c >> 6) & 1);
-    const int64_t bm = c >> 7;
-    const int mt = (int)(bm % MT), b = (int)(bm / MT);
-    const int m = mt * 32 + (l & 31);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + b * 32 + 16 * (l >> 5) + 8 * i);
-    xf[c] = v;
-  }
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int total = (K / 32) * MT * 128;
+  if (c >= total) return;
+  const int l = c & 63, i = (c >> 6) & 1, bm = c >> 7;
+  const int mt = bm % MT, b = bm / MT;
+  const int m = mt * 32 + (l & 31);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (m < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + b * 32 + 16 * (l >> 5) + 8 * i);
+  xf[c] = v;
 }
 
 // ============================================================================ dispatch
@@ -829,12 +823,15 @@ constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + argmax keys 
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
-  const int64_t S = n / kStrip, P = (S + 1) / 2, RK = k / kRecK, U = P * RK;
+  const int64_t S = n / kStrip, P = (S + 1) / 2, RK = k / kRecK;
+  const int64_t mt = m >= 16 ? (m + 31) / 32 : 0;
+  const int64_t U = P * RK;
   // one 8-wave workgroup per compute unit, every slice resident at once
   int64_t G = num_cu;
   if (G > U) G = U;
   if (G < 1) G = 1;
   pl.G = (int)G;
+  pl.U = (int)U;
   // The counter region has the same place and size for every shape (any
   // shape's tile counters, the argmax keys and the done counter), so a
   // workspace shared by calls of different shapes never holds old partial
@@ -845,7 +842,6 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   pl.off_part = kStateBytes;
   const size_t part_bytes = (size_t)2 * G * m * 64 * 4;
   pl.off_xf = (pl.off_part + part_bytes + 255) & ~size_t(255);
-  const int64_t mt = m >= 16 ? (m + 31) / 32 : 0;
   pl.ws_bytes = pl.off_xf + (size_t)mt * 32 * k * 2;
   return pl;
 }
@@ -855,8 +851,7 @@ hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s) {
   if (!k.fn) return hipErrorInvalidValue;
   if (k.mt > 0) {
     const int64_t chunks = (int64_t)(p.K / 32) * k.mt * 128;
-    const int64_t want = (chunks + 255) / 256;
-    const int blocks = (int)(want < 2048 ? want : 2048);
+    const int blocks = (int)((chunks + 255) / 256);
     hipLaunchKernelGGL(xfrag_kernel, dim3(blocks), dim3(256), 0, s, p.x, p.M, p.K, k.mt, p.xf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -40,7 +40,7 @@ struct GemmParams {
 };
 
 struct GemmPlan {
-  int G;
+  int G, U;
   size_t ws_bytes;
   size_t off_cnt, off_part, off_keys, off_done, off_xf;
 };
