@@ -58,35 +58,54 @@ int num_cu() {
 
 w12_status st(hipError_t e) { return e == hipSuccess ? W12_OK : W12_EHIP; }
 
+// Workspace of a call: the largest of its launches' plans (rows are split
+// into launches of at most w12::kRowsPerLaunch).
+size_t gemm_ws_bytes(int64_t n, int64_t k, int64_t m, int cu) {
+  size_t need = 0;
+  for (int64_t m0 = 0; m0 < m; m0 += w12::kRowsPerLaunch) {
+    const int64_t mc = m - m0 < w12::kRowsPerLaunch ? m - m0 : w12::kRowsPerLaunch;
+    const size_t b = w12::plan_gemm(n, k, mc, cu).ws_bytes;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
 w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
                     int32_t* idx, float* maxval, void* ws, size_t ws_bytes, hipStream_t s,
                     int epi) {
   const int cu = num_cu();
   if (cu <= 0) return W12_EHIP;
-  const w12::GemmPlan pl = w12::plan_gemm(w->n, w->k, m, cu);
-  if (!ws || ws_bytes < pl.ws_bytes) return ws ? W12_ENOSPC : W12_EINVAL;
+  if (!ws) return W12_EINVAL;
+  if (ws_bytes < gemm_ws_bytes(w->n, w->k, m, cu)) return W12_ENOSPC;
   char* base = static_cast<char*>(ws);
-  w12::GemmParams p{};
-  p.w = args_of(w);
-  p.x = x;
-  p.M = (int)m;
-  p.N = (int)w->n;
-  p.K = (int)w->k;
-  p.RK = (int)(w->k / 256);
-  p.S = (int)(w->n / 32);
-  p.P = (p.S + 1) / 2;
-  p.U = pl.U;
-  p.G = pl.G;
-  p.y = y;
-  p.ytype = ytype;
-  p.part = reinterpret_cast<float*>(base + pl.off_part);
-  p.xf = reinterpret_cast<uint4*>(base + pl.off_xf);
-  p.tile_cnt = reinterpret_cast<uint32_t*>(base + pl.off_cnt);
-  p.keys = reinterpret_cast<unsigned long long*>(base + pl.off_keys);
-  p.done = reinterpret_cast<uint32_t*>(base + pl.off_done);
-  p.idx = idx;
-  p.maxval = maxval;
-  return st(w12::launch_gemm(p, epi, s));
+  const size_t y_row = (size_t)w->n * (ytype == W12_Y_F32 ? 4 : 2);
+  for (int64_t m0 = 0; m0 < m; m0 += w12::kRowsPerLaunch) {
+    const int64_t mc = m - m0 < w12::kRowsPerLaunch ? m - m0 : w12::kRowsPerLaunch;
+    const w12::GemmPlan pl = w12::plan_gemm(w->n, w->k, mc, cu);
+    w12::GemmParams p{};
+    p.w = args_of(w);
+    p.x = x + m0 * w->k;
+    p.M = (int)mc;
+    p.N = (int)w->n;
+    p.K = (int)w->k;
+    p.RK = (int)(w->k / 256);
+    p.S = (int)(w->n / 32);
+    p.P = pl.P;
+    p.U = pl.U;
+    p.G = pl.G;
+    p.y = y ? static_cast<void*>(static_cast<char*>(y) + m0 * y_row) : nullptr;
+    p.ytype = ytype;
+    p.part = reinterpret_cast<float*>(base + pl.off_part);
+    p.xf = reinterpret_cast<uint4*>(base + pl.off_xf);
+    p.tile_cnt = reinterpret_cast<uint32_t*>(base + pl.off_cnt);
+    p.keys = reinterpret_cast<unsigned long long*>(base + pl.off_keys);
+    p.done = reinterpret_cast<uint32_t*>(base + pl.off_done);
+    p.idx = idx ? idx + m0 : nullptr;
+    p.maxval = maxval ? maxval + m0 : nullptr;
+    const w12_status r = st(w12::launch_gemm(p, epi, s));
+    if (r != W12_OK) return r;
+  }
+  return W12_OK;
 }
 
 }  // namespace
@@ -141,7 +160,7 @@ w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
   if (!bytes || !shape_ok(n, k) || m < 1 || m > kMaxRows) return W12_EINVAL;
   const int cu = num_cu();
   if (cu <= 0) return W12_EHIP;
-  *bytes = w12::plan_gemm(n, k, m, cu).ws_bytes;
+  *bytes = gemm_ws_bytes(n, k, m, cu);
   return W12_OK;
 }
 

@@ -169,19 +169,23 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
 constexpr int kDeviceScope = 16;  // sc1 cache-policy bit: coherent across XCDs
 
 // Partial sums: slot (2g or 2g+1: the workgroup's first or last tile) x row
-// x 64 channels.
+// x TC channels of the tile.
+template <int TC>
 __device__ __forceinline__ uint32_t partial_off(const GemmParams& a, int slot, int m, int c4) {
-  return (uint32_t)(((slot * a.M + m) * 64 + c4) * 4);
+  return (uint32_t)(((slot * a.M + m) * TC + c4) * 4);
 }
+template <int TC>
 __device__ __forceinline__ rsrc_t partial_rsrc(const GemmParams& a) {
-  return make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * 256u);
+  return make_rsrc(a.part, (uint32_t)(2 * a.G) * (uint32_t)a.M * (uint32_t)(TC * 4));
 }
+template <int TC>
 __device__ __forceinline__ void store_partial(const GemmParams& a, int slot, int m, int c4, float4 v) {
   const u32x4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(d, partial_rsrc(a), partial_off(a, slot, m, c4), 0, kDeviceScope);
+  __builtin_amdgcn_raw_buffer_store_b128(d, partial_rsrc<TC>(a), partial_off<TC>(a, slot, m, c4), 0, kDeviceScope);
 }
+template <int TC>
 __device__ __forceinline__ float4 load_partial(const GemmParams& a, int slot, int m, int c4) {
-  const u32x4 d = bload4<kDeviceScope>(partial_rsrc(a), partial_off(a, slot, m, c4), 0);
+  const u32x4 d = bload4<kDeviceScope>(partial_rsrc<TC>(a), partial_off<TC>(a, slot, m, c4), 0);
   return make_float4(__uint_as_float(d.x), __uint_as_float(d.y), __uint_as_float(d.z), __uint_as_float(d.w));
 }
 // Every thread's earlier global writes and atomics are acknowledged, then
@@ -203,9 +207,16 @@ __device__ __forceinline__ int partial_slot(int g, int p, int U, int G, int RK) 
 }
 
 // Last contributor of a split tile sums the partials in slice order. Called
-// after writes_done_barrier(), once per split tile of the slice.
-template <int EPI>
-__device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_last) {
+// after writes_done_barrier(), once per split tile of the slice. NT threads,
+// TC channels per tile, CH float4 per thread per round; 16 consecutive
+// threads share a row (TC >= 64). The partials of 4 contributors x CH float4
+// are requested before any is added (missing contributors read through an
+// empty resource as zero), so a round costs one memory latency, not one per
+// load.
+template <int EPI, int NT, int TC, int CH>
+__device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_last) {
+  constexpr int Q = TC / 4;  // float4 per tile row
+  constexpr int kC = 4;      // contributors per round
   const int gf = owner_of(p * a.RK, a.U, a.G);
   const int gl = owner_of((p + 1) * a.RK - 1, a.U, a.G);
   if (tid == 0) {
@@ -214,13 +225,40 @@ __device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_la
   }
   __syncthreads();
   if (*s_last) {
-    for (int e = tid; e < ((a.M + 31) & ~31) * 16; e += kNT) {
-      const int m = e >> 4, c4 = (e & 15) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m < a.M) {
-        for (int gg = gf; gg <= gl; ++gg) v = f4add(v, load_partial(a, partial_slot(gg, p, a.U, a.G, a.RK), m, c4));
+    const rsrc_t rp = partial_rsrc<TC>(a), r0 = make_rsrc(a.part, 0u);
+    const int total = ((a.M + 31) & ~31) * Q;
+    for (int e0 = 0; e0 < total; e0 += NT * CH) {
+      uint32_t off[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int e = e0 + j * NT + tid;
+        off[j] = partial_off<TC>(a, 0, min(e / Q, a.M - 1), (e % Q) * 4);
       }
-      emit4<EPI>(a, tid, m, p * 64 + c4, v);
+      float4 v[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int gg = gf; gg <= gl; gg += kC) {
+        u32x4 d[kC][CH];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+          const bool ok = gg + c <= gl;
+          const uint32_t so = ok ? partial_off<TC>(a, partial_slot(gg + c, p, a.U, a.G, a.RK), 0, 0) : 0u;
+          const rsrc_t r = ok ? rp : r0;
+#pragma unroll
+          for (int j = 0; j < CH; ++j) d[c][j] = bload4<kDeviceScope>(r, off[j], so);
+        }
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+          for (int j = 0; j < CH; ++j)
+            v[j] = f4add(v[j], make_float4(__uint_as_float(d[c][j].x), __uint_as_float(d[c][j].y),
+                                           __uint_as_float(d[c][j].z), __uint_as_float(d[c][j].w)));
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int e = e0 + j * NT + tid;
+        emit4<EPI>(a, tid, e / Q, p * TC + (e % Q) * 4, v[j]);
+      }
     }
     if (tid == 0) atomicExch(&a.tile_cnt[p], 0u);
   }
@@ -230,14 +268,14 @@ __device__ void finish_split_tile(const GemmParams& a, int p, int tid, int* s_la
 // After the whole grid is done, the last workgroup turns keys into ids and
 // returns the keys and the done counter to zero (keys are read and cleared
 // with device-coherent atomics).
-template <int EPI>
-__device__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
+template <int EPI, int NT>
+__device__ __forceinline__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
   if constexpr (EPI == kEpiArgmax) {
     writes_done_barrier();
     if (tid == 0) *s_last = (atomicAdd(a.done, 1u) == (uint32_t)(a.G - 1)) ? 1 : 0;
     __syncthreads();
     if (*s_last) {
-      for (int m = tid; m < a.M; m += kNT) {
+      for (int m = tid; m < a.M; m += NT) {
         const unsigned long long k = atomicExch(&a.keys[m], 0ull);
         a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
         if (a.maxval) a.maxval[m] = key_float((uint32_t)(k >> 32));
@@ -251,15 +289,15 @@ __device__ void finish_grid(const GemmParams& a, int tid, int* s_last) {
 // shares with its neighbours were stored when those tiles ended; the hand-off
 // waits until now, so no memory round trip stalled the stream. Then, for the
 // argmax epilogue, the grid-wide key-to-id step.
-template <int EPI>
-__device__ void finish_slice(const GemmParams& a, int tid, int u0, int u1, int* s_last) {
+template <int EPI, int NT, int TC, int CH>
+__device__ __forceinline__ void finish_slice(const GemmParams& a, int tid, int u0, int u1, int* s_last) {
   const int RK = a.RK, p0 = u0 / RK, p1 = (u1 - 1) / RK;
   const bool s0 = u0 < u1 && tile_is_split(p0, u0, u1, RK);
   const bool s1 = u0 < u1 && p1 != p0 && tile_is_split(p1, u0, u1, RK);
   if (s0 || s1 || EPI == kEpiArgmax) writes_done_barrier();
-  if (s0) finish_split_tile<EPI>(a, p0, tid, s_last);
-  if (s1) finish_split_tile<EPI>(a, p1, tid, s_last);
-  finish_grid<EPI>(a, tid, s_last);
+  if (s0) finish_split_tile<EPI, NT, TC, CH>(a, p0, tid, s_last);
+  if (s1) finish_split_tile<EPI, NT, TC, CH>(a, p1, tid, s_last);
+  finish_grid<EPI, NT>(a, tid, s_last);
 }
 
 // (E_n - 15) << 7 in both 16-bit halves for this lane's channel, from the
@@ -393,36 +431,41 @@ template <int XQ>
 struct UnitLoads {
   const GemmParams& a;
   int u0, u1, wave, lane, RK, S;
-  uint32_t tile_bytes, eo_bytes, v_hi, v_lo, v_et;
+  uint32_t strip_bytes, v_hi, v_lo, v_et;
   rsrc_t r_esc;
 
+  // Each strip gets its own resource (empty when the strip or the unit does
+  // not exist), so every offset that may fall outside lives inside a range
+  // the hardware checks.
   __device__ __forceinline__ void issue_off(Slot<XQ>& s, const UnitIt& it) const {
-    const rsrc_t r = make_rsrc(a.w.esc_off, it.u < u1 ? eo_bytes : 0u);
-    const uint32_t b0 = ((uint32_t)(2 * it.p) * RK + it.r) * 8 + wave;
-    const u32x2 o0 = bload2(r, 0, b0 * 4);
-    const u32x2 o1 = bload2(r, 0, (b0 + 8 * RK) * 4);
-    s.off[0][0] = o0.x;
-    s.off[0][1] = o0.y;
-    s.off[1][0] = o1.x;
-    s.off[1][1] = o1.y;
-  }
-  __device__ __forceinline__ void issue_w(Slot<XQ>& s, const UnitIt& it) const {
-    const int p = it.p;
-    const bool live = it.u < u1, has0 = 2 * p < S, has1 = 2 * p + 1 < S;
-    const uint32_t bytes = (live && has0) ? (has1 ? 2 * tile_bytes : tile_bytes) : 0u;
-    const rsrc_t r_rec = make_rsrc(a.w.rec + (int64_t)(2 * p) * tile_bytes, bytes);
-    const uint32_t so = (uint32_t)it.r * kRecBytes;
+    const bool live = it.u < u1;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      s.hi[q] = bload4<kNonTemporal>(r_rec, v_hi, so + q * tile_bytes);
-      s.lo[q] = bload2<kNonTemporal>(r_rec, v_lo, so + q * tile_bytes);
+      const int sq = 2 * it.p + q;
+      const bool ok = live && sq < S;
+      const uint32_t b = ((uint32_t)sq * RK + it.r) * 8 + wave;
+      const rsrc_t r = make_rsrc(a.w.esc_off + (ok ? b : 0u), ok ? 8u : 0u);
+      const u32x2 o = bload2(r, 0, 0);
+      s.off[q][0] = o.x;
+      s.off[q][1] = o.y;
     }
+  }
+  __device__ __forceinline__ void issue_w(Slot<XQ>& s, const UnitIt& it) const {
+    const bool live = it.u < u1;
+    const uint32_t so = (uint32_t)it.r * kRecBytes;
     // window tops change per tile: fetched at a tile's first record and at
     // the slice's first unit
     const bool et_now = live && (it.r == 0 || it.u == u0);
-    const rsrc_t r_et = make_rsrc(a.w.e_top, et_now ? (uint32_t)a.N : 0u);
-    s.et[0] = bload1(r_et, v_et, (uint32_t)p * 64);
-    s.et[1] = bload1(r_et, v_et, (uint32_t)p * 64 + 32);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int sq = 2 * it.p + q;
+      const bool ok = live && sq < S, eo = et_now && sq < S;
+      const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
+      s.hi[q] = bload4<kNonTemporal>(r, v_hi, so);
+      s.lo[q] = bload2<kNonTemporal>(r, v_lo, so);
+      const rsrc_t re = make_rsrc(a.w.e_top + (eo ? sq : 0) * kStrip, eo ? (uint32_t)kStrip : 0u);
+      s.et[q] = bload1(re, v_et, 0);
+    }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ>& s, const UnitIt& it) const {
     const int p = it.p;
@@ -500,11 +543,10 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S,
-                             (uint32_t)RK * kRecBytes, (uint32_t)((a.w.nb + 1) * 4),
-                             (uint32_t)(wave * 1024 + lane * 16),
-                             (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
-                             make_rsrc(a.w.esc, 0xFFFFFFFFu)};
+  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
+                        (uint32_t)(wave * 1024 + lane * 16),
+                        (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                        make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t xf_bytes = (uint32_t)(MT * 32) * (uint32_t)a.K * 2u;
   const rsrc_t r_xf = make_rsrc(a.xf, xf_bytes);
   const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
@@ -557,7 +599,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       if (whole) {
         emit4<EPI>(a, tid, m, p * 64 + c4, v);
       } else if (m < a.M) {
-        store_partial(a, slot, m, c4, v);
+        store_partial<64>(a, slot, m, c4, v);
       }
     });
     lds_barrier();
@@ -622,7 +664,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
     flush(tile_open);
   }
-  finish_slice<EPI>(a, tid, u0, u1, &s_last);
+  finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ VALU path (m < 16)
@@ -649,12 +691,11 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
-  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S,
-                             (uint32_t)RK * kRecBytes, (uint32_t)((a.w.nb + 1) * 4),
-                             (uint32_t)(wave * 1024 + lane * 16),
-                             (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
-                             make_rsrc(a.w.esc, 0xFFFFFFFFu)};
-  const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0
+  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
+                        (uint32_t)(wave * 1024 + lane * 16),
+                        (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                        make_rsrc(a.w.esc, 0xFFFFFFFFu)};
+  const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0 (voffset past the range)
   const rsrc_t r_x = make_rsrc(a.x, x_bytes);
   const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
   const uint32_t plo = patch_lane_off(lane);
@@ -667,9 +708,9 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
 #pragma unroll
       for (int m = 0; m < XQ; ++m) {
-        const uint32_t so_x = m * row_bytes + (uint32_t)it.r * 512;
-        s.xv[m][0] = bload4(rx, v_x, so_x);
-        s.xv[m][1] = bload4(rx, v_x + 16, so_x);
+        const uint32_t vx = v_x + m * row_bytes, so_x = (uint32_t)it.r * 512;
+        s.xv[m][0] = bload4(rx, vx, so_x);
+        s.xv[m][1] = bload4(rx, vx + 16, so_x);
       }
     }
   };
@@ -696,7 +737,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       if (whole) {
         emit4<EPI>(a, tid, m, p * 64 + c4, v);
       } else if (m < a.M) {
-        store_partial(a, slot, m, c4, v);
+        store_partial<64>(a, slot, m, c4, v);
       }
     }
     lds_barrier();
@@ -744,9 +785,9 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
         u32x4 xl[XG][2];
 #pragma unroll
         for (int i = 0; i < XG; ++i) {
-          const uint32_t so_x = (m0 + i) * row_bytes + (uint32_t)cur.r * 512;
-          xl[i][0] = bload4(r_x, v_x, so_x);
-          xl[i][1] = bload4(r_x, v_x + 16, so_x);
+          const uint32_t vx = v_x + (m0 + i) * row_bytes, so_x = (uint32_t)cur.r * 512;
+          xl[i][0] = bload4(r_x, vx, so_x);
+          xl[i][1] = bload4(r_x, vx + 16, so_x);
         }
 #pragma unroll
         for (int i = 0; i < XG; ++i) {
@@ -762,7 +803,326 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
     flush(tile_open);
   }
-  finish_slice<EPI>(a, tid, u0, u1, &s_last);
+  finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
+}
+
+// ============================================================================ large-m path (m > 64)
+//
+// At a few hundred rows the MFMA work per weight byte is no longer small, and
+// x per record (m x 512 B) outweighs the record itself. Layout for that case:
+//  * One workgroup of 4 waves per compute unit (one wave per SIMD, so each
+//    wave has the full register file: the accumulators of two strips x all
+//    rows live in the accumulation registers).
+//  * Tile = 4 strips (128 channels); unit = one record of a tile; stream-K
+//    slices as above. A unit is walked in 4 stages of 64 k.
+//  * Wave (cg, kg) restores subtile 2h + kg of strips 2cg, 2cg + 1 in stage
+//    h: the per-wave restore and escape patch of the small-m kernel.
+//  * x of a stage (all rows x 64 k) is read from row-major x once per
+//    workgroup -- every wave instruction reads 8 whole 128-byte row pieces --
+//    and written to LDS rows of 144 bytes, double-buffered: the 16-byte pad
+//    keeps both the stores and the B-fragment reads free of bank conflicts.
+//    Rows >= m fall outside the x resource and read as zero.
+//  * At a tile end the two k halves are summed through LDS.
+
+constexpr int kBigNW = 4;                  // waves per workgroup
+constexpr int kBigNT = kBigNW * 64;
+constexpr int kBigTC = 4 * kStrip;         // channels per tile
+constexpr int kStageK = 64;                // k per stage
+constexpr int kStages = kRecK / kStageK;   // stages per record
+constexpr int kXRow = 2 * kStageK + 16;    // LDS bytes per x row of a stage
+constexpr int kBigMaxMT = 6;               // rows per launch <= 192
+
+template <int MT>
+struct BigLds {
+  static constexpr int kX = MT * 32 * kXRow;      // one stage buffer
+  static constexpr int kPatch = kBigNW * 4096;    // per-wave patch buffers
+  static constexpr int kRed = 2 * MT * 4 * 1024;  // 2 waves x MT x 4 float4 x 64 lanes
+  static constexpr int kBytes = 2 * kX + kPatch + kRed;
+};
+
+// Position in a slice: unit (tile, record) and stage.
+struct StageIt {
+  int u, p, r, h;
+  __device__ __forceinline__ void init(int u0, int RK) {
+    u = u0;
+    p = u0 / RK;
+    r = u0 - p * RK;
+    h = 0;
+  }
+  __device__ __forceinline__ void next(int RK) {
+    if (++h == kStages) {
+      h = 0;
+      ++u;
+      if (++r == RK) {
+        r = 0;
+        ++p;
+      }
+    }
+  }
+};
+
+// Per-stage loads of wave (cg, kg): subtile 2h + kg of strips 4p + 2cg + q.
+struct BigLoads {
+  const GemmParams& a;
+  int u0, u1, cg, kg, RK, S;
+  uint32_t strip_bytes, v_hi, v_lo, v_et;
+  rsrc_t r_esc;
+
+  __device__ __forceinline__ void issue_off(Slot<0>& s, const StageIt& it) const {
+    const bool live = it.u < u1;
+    const int t = 2 * it.h + kg;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int sq = 4 * it.p + 2 * cg + q;
+      const bool ok = live && sq < S;
+      const uint32_t b = ((uint32_t)sq * RK + it.r) * 8 + t;
+      const rsrc_t r = make_rsrc(a.w.esc_off + (ok ? b : 0u), ok ? 8u : 0u);
+      const u32x2 o = bload2(r, 0, 0);
+      s.off[q][0] = o.x;
+      s.off[q][1] = o.y;
+    }
+  }
+  __device__ __forceinline__ void issue_w(Slot<0>& s, const StageIt& it) const {
+    const bool live = it.u < u1;
+    const uint32_t t = 2 * it.h + kg, so = (uint32_t)it.r * kRecBytes;
+    const bool et_now = live && it.h == 0 && (it.r == 0 || it.u == u0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int sq = 4 * it.p + 2 * cg + q;
+      const bool ok = live && sq < S, eo = et_now && sq < S;
+      const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
+      s.hi[q] = bload4<kNonTemporal>(r, v_hi, so + t * 1024);
+      s.lo[q] = bload2<kNonTemporal>(r, v_lo, so + t * 512);
+      const rsrc_t re = make_rsrc(a.w.e_top + (eo ? sq : 0) * kStrip, eo ? (uint32_t)kStrip : 0u);
+      s.et[q] = bload1(re, v_et, 0);
+    }
+  }
+  __device__ __forceinline__ void issue_e(Slot<0>& s, int lane) const {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = s.off[q][0];
+      const int c = (int)(s.off[q][1] - o);
+      s.e[q] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u) * 4u, 0);
+    }
+  }
+};
+
+// Stage walk. The ring has one slot per stage of a unit, so one trip of the
+// loop is one unit with compile-time slots, and a tile can only end between
+// trips (the tile-end code is not repeated in every unrolled stage). Weight
+// loads run 2 stages ahead, escape offsets 3; x of stage s + 1 is loaded at
+// the start of stage s (before the weight loads, so waiting for it never
+// waits for them) and stored to LDS at its end; one barrier per stage.
+constexpr int kBigDepth = kStages - 2;
+
+template <int MT, typename XL, typename XS, typename TF, typename StepF>
+__device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, int u1, int RK, XL&& xload,
+                                         XS&& xstore, TF&& tile_end, StepF&& step) {
+  Slot<0> ring[kStages];
+  StageIt itO, itW, itX;
+  itO.init(u0, RK);
+  itW.init(u0, RK);
+  itX.init(u0, RK);
+  u32x4 xr[MT];
+  xload(xr, itX);
+  itX.next(RK);
+  L.issue_off(ring[0], itO);
+  itO.next(RK);
+  static_for<kBigDepth>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    L.issue_off(ring[j + 1], itO);
+    itO.next(RK);
+    L.issue_w(ring[j], itW);
+    L.issue_e(ring[j], lane);
+    itW.next(RK);
+  });
+  xstore(xr, 0);
+  lds_barrier();
+  auto iteration = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    xload(xr, itX);
+    itX.next(RK);
+    L.issue_off(ring[(k + kBigDepth + 1) % kStages], itO);
+    itO.next(RK);
+    L.issue_w(ring[(k + kBigDepth) % kStages], itW);
+    L.issue_e(ring[(k + kBigDepth) % kStages], lane);
+    itW.next(RK);
+    step(ring[k], k & 1);
+    xstore(xr, (k + 1) & 1);
+    lds_barrier();
+  };
+  // tile by tile: the inner loop carries the accumulators through MFMAs only
+  for (int u = u0; u < u1;) {
+    const int p = u / RK, ue = min(u1, (p + 1) * RK);
+    for (; u < ue; ++u) static_for<kStages>(iteration);
+    tile_end(p);
+  }
+}
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
+  using Lds = BigLds<MT>;
+  __shared__ __align__(16) char lds[Lds::kBytes];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = wave & 1, kg = wave >> 1;
+  const int g = logical_wg(blockIdx.x, a.G);
+  const int U = a.U, RK = a.RK, S = a.S;
+  const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
+  char* patch = lds + 2 * Lds::kX + wave * 4096;
+  float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
+
+  f32x16 acc[2][MT];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
+
+  const BigLoads L{a, u0, u1, cg, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
+                   (uint32_t)(kHiBytes + lane * 8), (uint32_t)(lane & 28), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
+  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
+  const uint32_t plo = patch_lane_off(lane);
+
+  // x staging: thread piece j = tid & 7 (16 B) of row 32 i + (tid >> 3)
+  const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
+  const uint32_t row32 = 64u * (uint32_t)a.K;  // bytes of 32 rows
+  const uint32_t v_x = (uint32_t)(tid >> 3) * 2u * (uint32_t)a.K + (uint32_t)(tid & 7) * 16u;
+  const uint32_t x_w = (uint32_t)(tid >> 3) * kXRow + (uint32_t)(tid & 7) * 16u;
+  auto xload = [&](u32x4 (&xr)[MT], const StageIt& it) __attribute__((always_inline)) {
+    const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
+    const uint32_t so = ((uint32_t)it.r * kRecK + (uint32_t)it.h * kStageK) * 2u;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xr[i] = bload4(rx, v_x + i * row32, so);
+  };
+  auto xstore = [&](const u32x4 (&xr)[MT], int buf) __attribute__((always_inline)) {
+    char* b = lds + buf * Lds::kX + x_w;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) *reinterpret_cast<u32x4*>(b + i * 32 * kXRow) = xr[i];
+  };
+  // B fragment of (mt, i2): x[mt*32 + lane%32][32 kg + 16 (lane/32) + 8 i2 ..]
+  const uint32_t x_r = (uint32_t)(lane & 31) * kXRow + 64u * kg + 32u * (uint32_t)(lane >> 5);
+
+  // ---- tile end: sum the two k halves, write or hand off
+  auto flush = [&](int p) __attribute__((always_inline)) {
+    const bool whole = !tile_is_split(p, u0, u1, RK);
+    const int slot = partial_slot(g, p, U, a.G, RK);
+    unsigned long long best[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) best[mt] = 0;
+    static_for<2>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      if (kg == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4*>(red + (((cg * MT + mt) * 4 + rb) * 64 + lane) * 4) =
+                make_float4(acc[q][mt][4 * rb], acc[q][mt][4 * rb + 1], acc[q][mt][4 * rb + 2],
+                            acc[q][mt][4 * rb + 3]);
+      }
+      lds_barrier();
+      if (kg == 0) {
+        const int c0 = (2 * cg + q) * kStrip + 4 * (lane >> 5);  // channel within the tile
+        const bool cvalid = p * kBigTC + c0 < a.N;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = mt * 32 + (lane & 31);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const float4 o = *reinterpret_cast<const float4*>(red + (((cg * MT + mt) * 4 + rb) * 64 + lane) * 4);
+            const float4 v = make_float4(acc[q][mt][4 * rb] + o.x, acc[q][mt][4 * rb + 1] + o.y,
+                                         acc[q][mt][4 * rb + 2] + o.z, acc[q][mt][4 * rb + 3] + o.w);
+            const int c = c0 + 8 * rb, n = p * kBigTC + c;
+            if (!whole) {
+              if (m < a.M && cvalid) store_partial<kBigTC>(a, slot, m, c, v);
+            } else if constexpr (EPI == kEpiY) {
+              if (m < a.M && cvalid) {
+                if (a.ytype == 0) {
+                  *reinterpret_cast<float4*>(static_cast<float*>(a.y) + (int64_t)m * a.N + n) = v;
+                } else {
+                  const uint32_t lo = f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+                  const uint32_t hi = f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+                  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + (int64_t)m * a.N + n) =
+                      make_uint2(lo, hi);
+                }
+              }
+            } else {
+              if (cvalid) {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const unsigned long long key = ((unsigned long long)float_key(vv[i]) << 32) |
+                                                 (uint32_t)(0xFFFFFFFFu - (uint32_t)(n + i));
+                  best[mt] = key > best[mt] ? key : best[mt];
+                }
+              }
+            }
+          }
+        }
+      }
+      if (q == 0) lds_barrier();
+    });
+    if constexpr (EPI == kEpiArgmax) {
+      if (whole && kg == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = mt * 32 + (lane & 31);
+          const uint32_t lo = (uint32_t)best[mt], hi = (uint32_t)(best[mt] >> 32);
+          const unsigned long long o = ((unsigned long long)(uint32_t)__shfl_xor((int)hi, 32, 64) << 32) |
+                                       (uint32_t)__shfl_xor((int)lo, 32, 64);
+          const unsigned long long b = o > best[mt] ? o : best[mt];
+          if (lane < 32 && m < a.M && b) atomicMax(&a.keys[m], b);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
+  };
+
+  StageIt cur;
+  cur.init(u0, RK);
+  uint32_t bias[2] = {0u, 0u};
+  auto step = [&](const Slot<0>& s, int buf) __attribute__((always_inline)) {
+    const int sw = 4 * cur.p + 2 * cg;
+    const bool has0 = sw < S, has1 = sw + 1 < S;
+    if (cur.h == 0 && (cur.r == 0 || cur.u == u0)) {  // new tile: this slot carries its window tops
+      bias[0] = lane_bias2(s.et[0], et_shift);
+      bias[1] = lane_bias2(s.et[1], et_shift);
+    }
+    // all B fragments of the stage are requested before the restore, so
+    // their LDS latency hides behind it
+    const char* xb = lds + buf * Lds::kX + x_r;
+    bf16x8 bq[2][MT];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) bq[i2][mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 32 * kXRow + 16 * i2);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t P[2][8];
+    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
+    static_for<2>([&](auto ic) {
+      constexpr int i2 = decltype(ic)::value;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{P[0][4 * i2], P[0][4 * i2 + 1], P[0][4 * i2 + 2], P[0][4 * i2 + 3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{P[1][4 * i2], P[1][4 * i2 + 1], P[1][4 * i2 + 2], P[1][4 * i2 + 3]});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[i2][mt], acc[0][mt], 0, 0, 0);
+        acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[i2][mt], acc[1][mt], 0, 0, 0);
+      }
+    });
+    cur.next(RK);
+  };
+
+  if (u0 < u1) walk_big<MT>(L, lane, u0, u1, RK, xload, xstore, flush, step);
+  finish_slice<EPI, kBigNT, kBigTC, 8>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ x rearrangement
@@ -787,32 +1147,36 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__
 
 struct KernelSel {
   const void* fn;
-  int mt;  // 32-row tiles of the MFMA path (0: VALU path)
+  int mt;       // 32-row tiles of x fragments to prepare (0: none)
+  int threads;  // workgroup size
 };
 
 template <int EPI>
 KernelSel select_kernel(int M) {
-  if (M >= 16) {
+  if (M > kSmallMaxRows) {
     switch ((M + 31) / 32) {
-#define W12_MFMA(MT) \
-  case MT:           \
-    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<MT, EPI>), MT};
-      W12_MFMA(1) W12_MFMA(2) W12_MFMA(3) W12_MFMA(4)
-      W12_MFMA(5) W12_MFMA(6) W12_MFMA(7) W12_MFMA(8)
-#undef W12_MFMA
+#define W12_BIG(MT) \
+  case MT:          \
+    return {reinterpret_cast<const void*>(&gemm_big_kernel<MT, EPI>), 0, kBigNT};
+      W12_BIG(3) W12_BIG(4) W12_BIG(5) W12_BIG(6)
+#undef W12_BIG
       default:
-        return {nullptr, 0};
+        return {nullptr, 0, 0};
     }
+  }
+  if (M >= 16) {
+    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI>), 1, kNT};
+    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI>), 2, kNT};
   }
   const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   switch (mv) {
 #define W12_VALU(MV) \
   case MV:           \
-    return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI>), 0};
+    return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI>), 0, kNT};
     W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(16)
 #undef W12_VALU
     default:
-      return {nullptr, 0};
+      return {nullptr, 0, 0};
   }
 }
 
@@ -823,15 +1187,18 @@ constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + argmax keys 
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
-  const int64_t S = n / kStrip, P = (S + 1) / 2, RK = k / kRecK;
-  const int64_t mt = m >= 16 ? (m + 31) / 32 : 0;
+  const bool big = m > kSmallMaxRows;
+  const int64_t tc = big ? kBigTC : 2 * kStrip;
+  const int64_t S = n / kStrip, sp = tc / kStrip, P = (S + sp - 1) / sp, RK = k / kRecK;
+  const int64_t mt = (!big && m >= 16) ? (m + 31) / 32 : 0;
   const int64_t U = P * RK;
-  // one 8-wave workgroup per compute unit, every slice resident at once
+  // one workgroup per compute unit, every slice resident at once
   int64_t G = num_cu;
   if (G > U) G = U;
   if (G < 1) G = 1;
   pl.G = (int)G;
   pl.U = (int)U;
+  pl.P = (int)P;
   // The counter region has the same place and size for every shape (any
   // shape's tile counters, the argmax keys and the done counter), so a
   // workspace shared by calls of different shapes never holds old partial
@@ -840,7 +1207,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   pl.off_keys = kCounterBytes;
   pl.off_done = kCounterBytes + 256 * 8;
   pl.off_part = kStateBytes;
-  const size_t part_bytes = (size_t)2 * G * m * 64 * 4;
+  const size_t part_bytes = (size_t)2 * G * m * tc * 4;
   pl.off_xf = (pl.off_part + part_bytes + 255) & ~size_t(255);
   pl.ws_bytes = pl.off_xf + (size_t)mt * 32 * k * 2;
   return pl;
@@ -857,7 +1224,7 @@ hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   void* args[] = {const_cast<GemmParams*>(&p)};
-  return hipLaunchKernel(k.fn, dim3(p.G), dim3(kNT), args, 0, s);
+  return hipLaunchKernel(k.fn, dim3(p.G), dim3(k.threads), args, 0, s);
 }
 
 }  // namespace w12

@@ -16,22 +16,28 @@ struct MatrixArgs {
 
 enum Epilogue { kEpiY = 0, kEpiArgmax = 1 };
 
+// Rows up to kSmallMaxRows run the small-m kernels (64-channel tiles); more
+// rows, up to kRowsPerLaunch per launch, the large-m kernel (128-channel
+// tiles). Larger m is split into launches of kRowsPerLaunch rows.
+constexpr int kSmallMaxRows = 64;
+constexpr int kRowsPerLaunch = 192;
+
 // One verify GEMM (or LM head) launch. Work is split stream-K style: a unit
-// is one record of a 64-channel tile (two 32-channel strips), units run
-// tile-major, and workgroup g owns units [g*U/G, (g+1)*U/G).
+// is one record of a tile (2 strips of 32 channels for small m, 4 for large
+// m), units run tile-major, and workgroup g owns units [g*U/G, (g+1)*U/G).
 struct GemmParams {
   MatrixArgs w;
   const uint16_t* x;
   int M, N, K;
   int RK;  // records per strip = K / 256
   int S;   // strips = N / 32
-  int P;   // tiles = ceil(S / 2)
+  int P;   // tiles = ceil(S / strips per tile)
   int U;   // units = P * RK
   int G;   // workgroups
   void* y;
   int ytype;
   uint4* xf;              // x rearranged into MFMA B fragments (m >= 16)
-  float* part;            // [2G][M][64] split-tile partial sums
+  float* part;            // [2G][M][tile channels] split-tile partial sums
   uint32_t* tile_cnt;     // [P] arrival counters, zero between calls
   unsigned long long* keys;  // [M] argmax keys, zero between calls
   uint32_t* done;         // [1] finished-workgroup counter, zero between calls
@@ -40,11 +46,12 @@ struct GemmParams {
 };
 
 struct GemmPlan {
-  int G, U;
+  int G, U, P;
   size_t ws_bytes;
   size_t off_cnt, off_part, off_keys, off_done, off_xf;
 };
 
+// Plan of one launch (m <= kRowsPerLaunch).
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu);
 
 hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s);
