@@ -835,7 +835,7 @@ constexpr int kBigMaxMT = 6;               // rows per launch <= 192
 template <int MT>
 struct BigLds {
   static constexpr int kX = MT * 32 * kXRow;      // one stage buffer
-  static constexpr int kPatch = kBigNW * 4096;    // per-wave patch buffers
+  static constexpr int kPatch = kBigNW * 3 * 2048;  // per-wave patch buffers
   static constexpr int kRed = 2 * MT * 4 * 1024;  // 2 waves x MT x 4 float4 x 64 lanes
   static constexpr int kBytes = 2 * kX + kPatch + kRed;
 };
@@ -861,6 +861,15 @@ struct StageIt {
   }
 };
 
+// Loads of one stage for one wave.
+struct BigSlot {
+  uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
+  u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
+  u32x2 lo[2];         // their low nibbles
+  uint32_t et[2];      // dword holding the lane's channel's window top (tile starts)
+  uint32_t e[2][2];    // escape entries number lane and lane + 64 of the block
+};
+
 // Per-stage loads of wave (cg, kg): subtile 2h + kg of strips 4p + 2cg + q.
 struct BigLoads {
   const GemmParams& a;
@@ -868,7 +877,7 @@ struct BigLoads {
   uint32_t strip_bytes, v_hi, v_lo, v_et;
   rsrc_t r_esc;
 
-  __device__ __forceinline__ void issue_off(Slot<0>& s, const StageIt& it) const {
+  __device__ __forceinline__ void issue_off(BigSlot& s, const StageIt& it) const {
     const bool live = it.u < u1;
     const int t = 2 * it.h + kg;
 #pragma unroll
@@ -882,7 +891,7 @@ struct BigLoads {
       s.off[q][1] = o.y;
     }
   }
-  __device__ __forceinline__ void issue_w(Slot<0>& s, const StageIt& it) const {
+  __device__ __forceinline__ void issue_w(BigSlot& s, const StageIt& it) const {
     const bool live = it.u < u1;
     const uint32_t t = 2 * it.h + kg, so = (uint32_t)it.r * kRecBytes;
     const bool et_now = live && it.h == 0 && (it.r == 0 || it.u == u0);
@@ -897,28 +906,79 @@ struct BigLoads {
       s.et[q] = bload1(re, v_et, 0);
     }
   }
-  __device__ __forceinline__ void issue_e(Slot<0>& s, int lane) const {
+  __device__ __forceinline__ void issue_e(BigSlot& s, int lane) const {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const uint32_t o = s.off[q][0];
       const int c = (int)(s.off[q][1] - o);
-      s.e[q] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u) * 4u, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s.e[q][h] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane + 64 * h, c - 1) : 0u) * 4u, 0);
     }
   }
 };
 
+// Per-wave patch region: two 2 KB strip buffers, then 2 KB where the stores of
+// a block without entries land, so the patch has no branch.
+constexpr int kBigPatchStride = 3 * 2048;
+
+// Restore of the lane's 2 x 16 weights of a stage and the escape patch for
+// the first 128 entries of each block, without a branch: every lane stores
+// one entry per 64 (lanes past the count hold the last entry again and
+// rewrite its slot with the same value), and the stores of an empty block go
+// to the drop buffer. Blocks with more entries finish in restore_big_rest.
+__device__ __forceinline__ void restore_big(const BigSlot& s, uint32_t bias0, uint32_t bias1, int cnt0, int cnt1,
+                                            char* patch, uint32_t plo, uint32_t (&P)[2][8]) {
+  decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y}, bias0, P[0]);
+  decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y}, bias1, P[1]);
+  patch_store(patch, plo, P[0]);
+  patch_store(patch + 2048, plo, P[1]);
+  wave_lds_order();
+  const uint32_t base[2] = {cnt0 > 0 ? 0u : 4096u, cnt1 > 0 ? 2048u : 4096u};
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t e = s.e[q][h];
+      const uint32_t at = base[q] + (((e << 6) & 0x600u) | ((e >> 1) & 0x1F0u) | ((e << 1) & 0xEu));
+      *reinterpret_cast<uint16_t*>(patch + at) = esc_bits(e);
+    }
+  wave_lds_order();
+  patch_load(patch, plo, P[0]);
+  patch_load(patch + 2048, plo, P[1]);
+}
+// Entries 128 and on of blocks that have them (rare): a second patch pass.
+__device__ __forceinline__ void restore_big_rest(const BigSlot& s, int cnt0, int cnt1, char* patch, uint32_t plo,
+                                                 int lane, rsrc_t r_esc, uint32_t (&P)[2][8]) {
+  if (max(cnt0, cnt1) > 128) {
+    wave_lds_order();
+    patch_store(patch, plo, P[0]);
+    patch_store(patch + 2048, plo, P[1]);
+    wave_lds_order();
+    const int cq[2] = {cnt0, cnt1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = s.off[q][0];
+      for (int j = 128 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
+    }
+    wave_lds_order();
+    patch_load(patch, plo, P[0]);
+    patch_load(patch + 2048, plo, P[1]);
+  }
+}
+
 // Stage walk. The ring has one slot per stage of a unit, so one trip of the
 // loop is one unit with compile-time slots, and a tile can only end between
-// trips (the tile-end code is not repeated in every unrolled stage). Weight
-// loads run 2 stages ahead, escape offsets 3; x of stage s + 1 is loaded at
-// the start of stage s (before the weight loads, so waiting for it never
-// waits for them) and stored to LDS at its end; one barrier per stage.
+// trips. Weight loads run 2 stages ahead, escape offsets 3; x of stage s + 1
+// is loaded at the start of stage s (before the weight loads, so waiting for
+// it never waits for them) and stored to LDS at its end; one barrier per
+// stage.
 constexpr int kBigDepth = kStages - 2;
 
 template <int MT, typename XL, typename XS, typename TF, typename StepF>
 __device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, int u1, int RK, XL&& xload,
                                          XS&& xstore, TF&& tile_end, StepF&& step) {
-  Slot<0> ring[kStages];
+  BigSlot ring[kStages];
   StageIt itO, itW, itX;
   itO.init(u0, RK);
   itW.init(u0, RK);
@@ -947,8 +1007,7 @@ __device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, in
     L.issue_w(ring[(k + kBigDepth) % kStages], itW);
     L.issue_e(ring[(k + kBigDepth) % kStages], lane);
     itW.next(RK);
-    step(ring[k], k & 1);
-    xstore(xr, (k + 1) & 1);
+    step(ring[k], k & 1, xr);
     lds_barrier();
   };
   // tile by tile: the inner loop carries the accumulators through MFMAs only
@@ -971,7 +1030,7 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
   const int g = logical_wg(blockIdx.x, a.G);
   const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
-  char* patch = lds + 2 * Lds::kX + wave * 4096;
+  char* patch = lds + 2 * Lds::kX + wave * kBigPatchStride;
   float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
 
   f32x16 acc[2][MT];
@@ -1006,8 +1065,39 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
   // B fragment of (mt, i2): x[mt*32 + lane%32][32 kg + 16 (lane/32) + 8 i2 ..]
   const uint32_t x_r = (uint32_t)(lane & 31) * kXRow + 64u * kg + 32u * (uint32_t)(lane >> 5);
 
-  // ---- tile end: sum the two k halves, write or hand off
+  // MFMA operands of the previous stage: its products are issued during the
+  // next stage, interleaved with that stage's loads and restore. Zero
+  // operands (tile start) add exact zeros.
+  uint32_t Pp[2][8];
+  bf16x8 Bp[2][MT];
+  auto clear_pending = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Pp[q][i] = 0u;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Bp[i2][mt] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  };
+  auto mfma_pending = [&]() __attribute__((always_inline)) {
+    static_for<2>([&](auto ic) {
+      constexpr int i2 = decltype(ic)::value;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{Pp[0][4 * i2], Pp[0][4 * i2 + 1], Pp[0][4 * i2 + 2], Pp[0][4 * i2 + 3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{Pp[1][4 * i2], Pp[1][4 * i2 + 1], Pp[1][4 * i2 + 2], Pp[1][4 * i2 + 3]});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, Bp[i2][mt], acc[0][mt], 0, 0, 0);
+        acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, Bp[i2][mt], acc[1][mt], 0, 0, 0);
+      }
+    });
+  };
+  clear_pending();
+
+  // ---- tile end: last products, sum the two k halves, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
+    mfma_pending();
+    clear_pending();
     const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
     unsigned long long best[MT];
@@ -1090,34 +1180,45 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
   StageIt cur;
   cur.init(u0, RK);
   uint32_t bias[2] = {0u, 0u};
-  auto step = [&](const Slot<0>& s, int buf) __attribute__((always_inline)) {
-    const int sw = 4 * cur.p + 2 * cg;
-    const bool has0 = sw < S, has1 = sw + 1 < S;
-    if (cur.h == 0 && (cur.r == 0 || cur.u == u0)) {  // new tile: this slot carries its window tops
-      bias[0] = lane_bias2(s.et[0], et_shift);
-      bias[1] = lane_bias2(s.et[1], et_shift);
-    }
-    // all B fragments of the stage are requested before the restore, so
-    // their LDS latency hides behind it
+  auto step = [&](const BigSlot& s, int buf, const u32x4 (&xr)[MT]) __attribute__((always_inline)) {
+    // tile start: this slot carries the window tops (empty loads read 0)
+    const uint32_t nt = (cur.h == 0 && (cur.r == 0 || cur.u == u0)) ? 0xFFFFFFFFu : 0u;
+    bias[0] = (lane_bias2(s.et[0], et_shift) & nt) | (bias[0] & ~nt);
+    bias[1] = (lane_bias2(s.et[1], et_shift) & nt) | (bias[1] & ~nt);
+    // strips past the last and units past the slice load empty offsets: 0 entries
+    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
+    const int cnt1 = __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0]));
+    // this stage's B fragments, then the previous stage's products while
+    // this stage restores
     const char* xb = lds + buf * Lds::kX + x_r;
     bf16x8 bq[2][MT];
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) bq[i2][mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 32 * kXRow + 16 * i2);
-    __builtin_amdgcn_sched_barrier(0);
+    mfma_pending();
     uint32_t P[2][8];
-    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
-    static_for<2>([&](auto ic) {
-      constexpr int i2 = decltype(ic)::value;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{P[0][4 * i2], P[0][4 * i2 + 1], P[0][4 * i2 + 2], P[0][4 * i2 + 3]});
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{P[1][4 * i2], P[1][4 * i2 + 1], P[1][4 * i2 + 2], P[1][4 * i2 + 3]});
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[i2][mt], acc[0][mt], 0, 0, 0);
-        acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[i2][mt], acc[1][mt], 0, 0, 0);
-      }
+    restore_big(s, bias[0], bias[1], cnt0, cnt1, patch, plo, P);
+    // one product per few restore instructions, so the matrix unit runs
+    // while the restore issues
+    static_for<4 * MT>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // DS
     });
+    // x of the next stage last: its loads have had the whole stage
+    __builtin_amdgcn_sched_barrier(0);
+    xstore(xr, buf ^ 1);
+    restore_big_rest(s, cnt0, cnt1, patch, plo, lane, L.r_esc, P);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Pp[q][i] = P[q][i];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Bp[i2][mt] = bq[i2][mt];
     cur.next(RK);
   };
 
