@@ -98,6 +98,10 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
+    ap.add_argument("--workload", choices=("block", "batched", "stack"), default="block",
+                    help="block: one 27B-class block + LM head at M=32 (the headline line); "
+                         "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
+                         "and 2%% outliers; stack: 64 blocks in sequence at M=32")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +121,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w12.lib()
+
+    if args.workload == "batched":
+        return run_batched(args, w12, synth, torch, dev)
+    if args.workload == "stack":
+        return run_stack(args, w12, synth, torch, dev)
 
     mats, pack_gbps = build_block(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
@@ -264,6 +273,133 @@ def main():
         "accepted": {"accept_len": int(acc[0]), "bonus": int(bonus[0])},
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def clone_packed(w12, pw):
+    """A distinct device copy of every buffer of a packed matrix."""
+    return w12.PackedW12(pw.n, pw.k, pw.records.clone(), pw.e_top.clone(), pw.esc_off.clone(),
+                         pw.esc.clone(), pw.n_esc)
+
+
+def time_events(fn, reps):
+    """Mean microseconds of fn() over reps launches, timed with events on the
+    current stream."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return 1000.0 * a.elapsed_time(b) / reps
+
+
+def run_batched(args, w12, synth, torch, dev):
+    """Batched verify (24 trees x 8 nodes = 192 rows): Wup 17408x5120 then
+    Wdown 5120x17408, 3% zeros and 2% x64 outliers, bf16 out. Each matrix is
+    held in enough distinct packed copies (>= 1 GiB in all) that every call
+    streams its weights from HBM, not from the 256 MB last-level cache."""
+    m = 192
+    mats = []
+    for name, n, k, idx in (("UP", FFN, HIDDEN, 1), ("DOWN", HIDDEN, FFN, 2)):
+        seed = 1_000_000 * 5 + idx
+        w = synth.weights_bf16(n, k, seed=seed, p_zero=0.03, p_outlier=0.02, device=dev)
+        pw = w12.w12_pack(w, check=True)
+        del w
+        x = synth.activations_bf16(m, k, seed=seed + 500, device=dev)
+        ncopy = max(2, -(-(1 << 30) // pw.nbytes()))
+        copies = [pw] + [clone_packed(w12, pw) for _ in range(ncopy - 1)]
+        y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        mats.append((name, copies, x, y))
+        log(f"packed {name}: {n}x{k}, {pw.n_esc} escapes ({pw.n_esc / (n * k):.4%}), {ncopy} copies")
+    ws = w12.workspace(max(w12.gemm_workspace_bytes(c[0].n, c[0].k, m) for _, c, _, _ in mats), dev)
+
+    def step(i):
+        for _, copies, x, y in mats:
+            w12.w12_gemm(copies[i % len(copies)], x, out=y, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    us = time_events(step, args.steps)
+    per = {}
+    for name, copies, x, y in mats:
+        per[name] = time_events(lambda i, c=copies, x=x, y=y: w12.w12_gemm(c[i % len(c)], x, out=y, ws=ws),
+                                max(8, args.steps))
+    nbytes = sum(gemm_bytes(c[0], m, 2) for _, c, _, _ in mats)
+    flops = sum(2.0 * m * c[0].n * c[0].k for _, c, _, _ in mats)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    tflops = flops / (us * 1e-6) / 1e12
+    line = {
+        "metric": "W12 batched verify GEMM effective HBM GB/s at M=192 rows",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "batched verify: Wup 17408x5120 + Wdown 5120x17408, M=192 rows, "
+                               "3% zeros + 2% x64 outliers, bf16 out, >= 1 GiB of rotated copies",
+                   "rows": m, "bytes_per_step": int(nbytes), "flops_per_step": flops},
+        "breakdown_us": {n: round(v, 2) for n, v in per.items()},
+        "roofline": {"hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+                     "mfma_bf16": {"achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_stack(args, w12, synth, torch, dev):
+    """64 blocks of the 27B-class shape in sequence at M=32 (about 33 GB of W12
+    records): every GEMM of a layer after the previous one, eager and as a
+    replayed graph."""
+    layers = 64
+    shapes = (("QKV", Q_OUT + 2 * KV_OUT, HIDDEN), ("O", HIDDEN, Q_OUT), ("UP", 2 * FFN, HIDDEN),
+              ("DOWN", HIDDEN, FFN))
+    mats = []
+    for li in range(layers):
+        row = []
+        for j, (name, n, k) in enumerate(shapes):
+            w = synth.weights_bf16(n, k, seed=1_000_000 * 3 + 1000 * li + j + 1, device=dev)
+            row.append(w12.w12_pack(w, check=li == 0))
+            del w
+        mats.append(row)
+        if li % 16 == 15:
+            log(f"packed {li + 1} layers")
+    xs = {k: synth.activations_bf16(M_ROWS, k, seed=1_000_000 * 3 + 500 + k, device=dev)
+          for k in {k for _, _, k in shapes}}
+    ys = {name: torch.empty(M_ROWS, n, dtype=torch.bfloat16, device=dev) for name, n, _ in shapes}
+    ws = w12.workspace(max(w12.gemm_workspace_bytes(n, k, M_ROWS) for _, n, k in shapes), dev)
+
+    def one_pass(_=0):
+        for row in mats:
+            for (name, n, k), pw in zip(shapes, row):
+                w12.w12_gemm(pw, xs[k], out=ys[name], ws=ws)
+
+    for _ in range(max(1, args.warmup)):
+        one_pass()
+    torch.cuda.synchronize()
+    reps = max(3, min(args.steps, 10))
+    eager_us = time_events(one_pass, reps)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_us = time_events(lambda i: graph.replay(), reps)
+    nbytes = sum(gemm_bytes(pw, M_ROWS, 2) for row in mats for pw in row)
+    best = min(eager_us, graph_us)
+    gbps = nbytes / (best * 1e-6) / 1e9
+    line = {
+        "metric": "W12 verify pass of a 64-layer 27B-class stack at M=32: effective HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": max(1, args.warmup),
+        "ms_per_step": round(best / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "64 x (Wq|Wk|Wv 8192x5120, Wo 5120x6144, Wgate|Wup 34816x5120, "
+                               "Wdown 5120x17408), all W12, M=32, layers in order",
+                   "rows": M_ROWS, "bytes_per_pass": int(nbytes), "layers": layers},
+        "eager_ms_per_pass": round(eager_us / 1000.0, 4), "graph_ms_per_pass": round(graph_us / 1000.0, 4),
+        "us_per_layer": round(best / layers, 2), "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
     }
     print(json.dumps(line), flush=True)
 
