@@ -78,6 +78,29 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
                                            kRawBufferWord3);
 }
+// Wave-uniform metadata (escape-block offsets, window tops) is read through
+// the scalar data cache: the loads leave the vector memory path to the weight
+// stream. The buffers are read-only for the whole launch.
+typedef __attribute__((address_space(4))) const uint32_t* cu32p;
+__device__ __forceinline__ cu32p scalar_view(const void* p) { return (cu32p)p; }
+
+// (E_n - 15) << 7 in both 16-bit halves for the lane's channel of strip sq:
+// the strip's 32 window tops come in as 8 scalar dwords; the lane takes dword
+// (lane & 31) / 4 and its byte lane & 3.
+__device__ __forceinline__ uint32_t strip_bias2(const uint8_t* e_top, int sq, bool ok, int lane) {
+  const cu32p c = scalar_view(e_top) + (ok ? sq : 0) * (kStrip / 4);
+  uint32_t d[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d[i] = c[i];
+  const int j = (lane >> 2) & 7;
+  const uint32_t d01 = (j & 1) ? d[1] : d[0], d23 = (j & 1) ? d[3] : d[2];
+  const uint32_t d45 = (j & 1) ? d[5] : d[4], d67 = (j & 1) ? d[7] : d[6];
+  const uint32_t d03 = (j & 2) ? d23 : d01, d47 = (j & 2) ? d67 : d45;
+  const uint32_t dw = (j & 4) ? d47 : d03;
+  const uint32_t e = __builtin_amdgcn_ubfe(dw, 8u * (uint32_t)(lane & 3), 8);
+  return ok ? e * 0x00800080u - 0x07800780u : 0u;
+}
+
 template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
@@ -300,14 +323,6 @@ __device__ __forceinline__ void finish_slice(const GemmParams& a, int tid, int u
   finish_grid<EPI, NT>(a, tid, s_last);
 }
 
-// (E_n - 15) << 7 in both 16-bit halves for this lane's channel, from the
-// dword of window tops holding it (channel 4j + (lane & 3) of the strip):
-// one bit-field extract and one 24-bit multiply-add.
-__device__ __forceinline__ uint32_t lane_bias2(uint32_t dw, uint32_t shift) {
-  const uint32_t e = __builtin_amdgcn_ubfe(dw, shift, 8);
-  return e * 0x00800080u - 0x07800780u;
-}
-
 // Per-wave patch buffer of one strip: 2 KB of restored weights laid out as
 // halfword k4 * 512 + k3 * 256 + c * 8 + (kk & 7) for weight (channel c,
 // subtile column kk = 16 k4 + 8 k3 + (kk & 7)). Lane c + 32 h writes its pairs
@@ -404,7 +419,6 @@ struct Slot {
   uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
   u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[2];         // their low nibbles
-  uint32_t et[2];      // dword holding the lane's channel's window top (tile starts)
   uint32_t e[2];       // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ > 0 ? XQ : 1][2];  // x operands that ride with the unit
 };
@@ -431,40 +445,36 @@ template <int XQ>
 struct UnitLoads {
   const GemmParams& a;
   int u0, u1, wave, lane, RK, S;
-  uint32_t strip_bytes, v_hi, v_lo, v_et;
+  uint32_t strip_bytes, v_hi, v_lo;
   rsrc_t r_esc;
 
-  // Each strip gets its own resource (empty when the strip or the unit does
-  // not exist), so every offset that may fall outside lives inside a range
-  // the hardware checks.
+  // Each strip gets its own record resource (empty when the strip or the unit
+  // does not exist), so every offset that may fall outside lives inside a
+  // range the hardware checks; scalar loads of missing strips or units read
+  // block 0 and are replaced by zero offsets.
   __device__ __forceinline__ void issue_off(Slot<XQ>& s, const UnitIt& it) const {
     const bool live = it.u < u1;
+    const cu32p c = scalar_view(a.w.esc_off);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int sq = 2 * it.p + q;
       const bool ok = live && sq < S;
-      const uint32_t b = ((uint32_t)sq * RK + it.r) * 8 + wave;
-      const rsrc_t r = make_rsrc(a.w.esc_off + (ok ? b : 0u), ok ? 8u : 0u);
-      const u32x2 o = bload2(r, 0, 0);
-      s.off[q][0] = o.x;
-      s.off[q][1] = o.y;
+      const uint32_t b = ok ? ((uint32_t)sq * RK + it.r) * 8 + wave : 0u;
+      const uint32_t o0 = c[b], o1 = c[b + 1];
+      s.off[q][0] = ok ? o0 : 0u;
+      s.off[q][1] = ok ? o1 : 0u;
     }
   }
   __device__ __forceinline__ void issue_w(Slot<XQ>& s, const UnitIt& it) const {
     const bool live = it.u < u1;
     const uint32_t so = (uint32_t)it.r * kRecBytes;
-    // window tops change per tile: fetched at a tile's first record and at
-    // the slice's first unit
-    const bool et_now = live && (it.r == 0 || it.u == u0);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int sq = 2 * it.p + q;
-      const bool ok = live && sq < S, eo = et_now && sq < S;
+      const bool ok = live && sq < S;
       const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
       s.hi[q] = bload4<kNonTemporal>(r, v_hi, so);
       s.lo[q] = bload2<kNonTemporal>(r, v_lo, so);
-      const rsrc_t re = make_rsrc(a.w.e_top + (eo ? sq : 0) * kStrip, eo ? (uint32_t)kStrip : 0u);
-      s.et[q] = bload1(re, v_et, 0);
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ>& s, const UnitIt& it) const {
@@ -545,11 +555,10 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
   const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
                         (uint32_t)(wave * 1024 + lane * 16),
-                        (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                        (uint32_t)(kHiBytes + wave * 512 + lane * 8),
                         make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t xf_bytes = (uint32_t)(MT * 32) * (uint32_t)a.K * 2u;
   const rsrc_t r_xf = make_rsrc(a.xf, xf_bytes);
-  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
   const uint32_t plo = patch_lane_off(lane);
   const uint32_t v_x = (uint32_t)lane * 16u;
 
@@ -623,9 +632,9 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     }
     const int p = cur.p;
     const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
-    if (cur.r == 0 || cur.u == u0) {  // new tile: this slot carries its window tops
-      bias[0] = lane_bias2(s.et[0], et_shift);
-      bias[1] = lane_bias2(s.et[1], et_shift);
+    if (cur.r == 0 || cur.u == u0) {  // new tile: window tops of its strips
+      bias[0] = strip_bias2(a.w.e_top, 2 * p, has0, lane);
+      bias[1] = strip_bias2(a.w.e_top, 2 * p + 1, has1, lane);
     }
     uint32_t P[2][8];
     restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
@@ -693,11 +702,10 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 
   const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
                         (uint32_t)(wave * 1024 + lane * 16),
-                        (uint32_t)(kHiBytes + wave * 512 + lane * 8), (uint32_t)(lane & 28),
+                        (uint32_t)(kHiBytes + wave * 512 + lane * 8),
                         make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0 (voffset past the range)
   const rsrc_t r_x = make_rsrc(a.x, x_bytes);
-  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
   const uint32_t plo = patch_lane_off(lane);
   // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
   const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
@@ -767,9 +775,9 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     }
     const int p = cur.p;
     const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
-    if (cur.r == 0 || cur.u == u0) {  // new tile: this slot carries its window tops
-      bias[0] = lane_bias2(s.et[0], et_shift);
-      bias[1] = lane_bias2(s.et[1], et_shift);
+    if (cur.r == 0 || cur.u == u0) {  // new tile: window tops of its strips
+      bias[0] = strip_bias2(a.w.e_top, 2 * p, has0, lane);
+      bias[1] = strip_bias2(a.w.e_top, 2 * p + 1, has1, lane);
     }
     uint32_t P[2][8];
     restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
@@ -866,7 +874,6 @@ struct BigSlot {
   uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
   u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[2];         // their low nibbles
-  uint32_t et[2];      // dword holding the lane's channel's window top (tile starts)
   uint32_t e[2][2];    // escape entries number lane and lane + 64 of the block
 };
 
@@ -874,36 +881,33 @@ struct BigSlot {
 struct BigLoads {
   const GemmParams& a;
   int u0, u1, cg, kg, RK, S;
-  uint32_t strip_bytes, v_hi, v_lo, v_et;
+  uint32_t strip_bytes, v_hi, v_lo;
   rsrc_t r_esc;
 
   __device__ __forceinline__ void issue_off(BigSlot& s, const StageIt& it) const {
     const bool live = it.u < u1;
     const int t = 2 * it.h + kg;
+    const cu32p c = scalar_view(a.w.esc_off);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int sq = 4 * it.p + 2 * cg + q;
       const bool ok = live && sq < S;
-      const uint32_t b = ((uint32_t)sq * RK + it.r) * 8 + t;
-      const rsrc_t r = make_rsrc(a.w.esc_off + (ok ? b : 0u), ok ? 8u : 0u);
-      const u32x2 o = bload2(r, 0, 0);
-      s.off[q][0] = o.x;
-      s.off[q][1] = o.y;
+      const uint32_t b = ok ? ((uint32_t)sq * RK + it.r) * 8 + t : 0u;
+      const uint32_t o0 = c[b], o1 = c[b + 1];
+      s.off[q][0] = ok ? o0 : 0u;
+      s.off[q][1] = ok ? o1 : 0u;
     }
   }
   __device__ __forceinline__ void issue_w(BigSlot& s, const StageIt& it) const {
     const bool live = it.u < u1;
     const uint32_t t = 2 * it.h + kg, so = (uint32_t)it.r * kRecBytes;
-    const bool et_now = live && it.h == 0 && (it.r == 0 || it.u == u0);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int sq = 4 * it.p + 2 * cg + q;
-      const bool ok = live && sq < S, eo = et_now && sq < S;
+      const bool ok = live && sq < S;
       const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
       s.hi[q] = bload4<kNonTemporal>(r, v_hi, so + t * 1024);
       s.lo[q] = bload2<kNonTemporal>(r, v_lo, so + t * 512);
-      const rsrc_t re = make_rsrc(a.w.e_top + (eo ? sq : 0) * kStrip, eo ? (uint32_t)kStrip : 0u);
-      s.et[q] = bload1(re, v_et, 0);
     }
   }
   __device__ __forceinline__ void issue_e(BigSlot& s, int lane) const {
@@ -1042,8 +1046,7 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
   const BigLoads L{a, u0, u1, cg, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
-                   (uint32_t)(kHiBytes + lane * 8), (uint32_t)(lane & 28), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
-  const uint32_t et_shift = 8u * (uint32_t)(lane & 3);
+                   (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t plo = patch_lane_off(lane);
 
   // x staging: thread piece j = tid & 7 (16 B) of row 32 i + (tid >> 3)
@@ -1183,8 +1186,9 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
   auto step = [&](const BigSlot& s, int buf, const u32x4 (&xr)[MT]) __attribute__((always_inline)) {
     // tile start: this slot carries the window tops (empty loads read 0)
     const uint32_t nt = (cur.h == 0 && (cur.r == 0 || cur.u == u0)) ? 0xFFFFFFFFu : 0u;
-    bias[0] = (lane_bias2(s.et[0], et_shift) & nt) | (bias[0] & ~nt);
-    bias[1] = (lane_bias2(s.et[1], et_shift) & nt) | (bias[1] & ~nt);
+    const int sw = 4 * cur.p + 2 * cg;
+    bias[0] = (strip_bias2(a.w.e_top, sw, sw < S, lane) & nt) | (bias[0] & ~nt);
+    bias[1] = (strip_bias2(a.w.e_top, sw + 1, sw + 1 < S, lane) & nt) | (bias[1] & ~nt);
     // strips past the last and units past the slice load empty offsets: 0 entries
     const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
     const int cnt1 = __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0]));
