@@ -7,7 +7,8 @@
 // deterministic. The LM-head variant keeps the logits in registers and emits
 // only the greedy token (section 1.1: the target's argmax).
 //
-// gfx950 design (HBM-bound at every m this kernel serves):
+// gfx950 design for m <= 64 (HBM-bound; the layout for more rows is described
+// at the large-m kernel below):
 //  * Tile = 64 output channels (a pair of 32-channel strips). Unit = one
 //    256-k record of a tile (2 x 12 KB). Units run tile-major; workgroup g
 //    owns the contiguous slice [g*U/G, (g+1)*U/G) (stream-K). A tile split
@@ -20,7 +21,7 @@
 //  * Loads run D units ahead of the arithmetic and are always issued
 //    unconditionally; the loop has no barrier that waits on vector memory,
 //    so the next units' loads stay in flight across every barrier.
-//  * m >= 16: bf16 MFMA 32x32x16, weights = A, x = B. The B fragments come
+//  * 16 <= m <= 64: bf16 MFMA 32x32x16, weights = A, x = B. The B fragments come
 //    from a copy of x rearranged once per call so that every fragment load
 //    is one contiguous 1 KB per wave (xfrag_kernel).
 //  * m < 16: lanes own channels, fdot2 against x rows read from memory
@@ -28,6 +29,8 @@
 //  * Escapes (~1% of weights here): restored pairs go through a per-wave LDS
 //    buffer, the lanes holding the block's escape entries overwrite their
 //    slots, and the pairs are read back -- all synchronised within the wave.
+//  * Escape-block offsets and window tops are wave-uniform and come through
+//    the scalar data cache.
 #include <atomic>
 #include <type_traits>
 #include <utility>
@@ -818,35 +821,23 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 //
 // At a few hundred rows the MFMA work per weight byte is no longer small, and
 // x per record (m x 512 B) outweighs the record itself. Layout for that case:
-//  * One workgroup of 4 waves per compute unit (one wave per SIMD, so each
-//    wave has the full register file: the accumulators of two strips x all
-//    rows live in the accumulation registers).
 //  * Tile = 4 strips (128 channels); unit = one record of a tile; stream-K
-//    slices as above. A unit is walked in 4 stages of 64 k.
-//  * Wave (cg, kg) restores subtile 2h + kg of strips 2cg, 2cg + 1 in stage
-//    h: the per-wave restore and escape patch of the small-m kernel.
+//    slices and the fixed-order hand-off as above. A unit is walked in 4
+//    stages of 64 k.
+//  * 8 waves, two per SIMD: wave (s, kg) restores subtile 2h + kg of strip s
+//    in stage h (the per-wave restore and escape patch of the small-m kernel)
+//    and holds one strip x all M-tiles of accumulators.
 //  * x of a stage (all rows x 64 k) is read from row-major x once per
 //    workgroup -- every wave instruction reads 8 whole 128-byte row pieces --
 //    and written to LDS rows of 144 bytes, double-buffered: the 16-byte pad
 //    keeps both the stores and the B-fragment reads free of bank conflicts.
 //    Rows >= m fall outside the x resource and read as zero.
-//  * At a tile end the two k halves are summed through LDS.
+//  * At a tile end the two k halves of each strip are summed through LDS.
 
-constexpr int kBigNW = 4;                  // waves per workgroup
-constexpr int kBigNT = kBigNW * 64;
 constexpr int kBigTC = 4 * kStrip;         // channels per tile
 constexpr int kStageK = 64;                // k per stage
 constexpr int kStages = kRecK / kStageK;   // stages per record
 constexpr int kXRow = 2 * kStageK + 16;    // LDS bytes per x row of a stage
-constexpr int kBigMaxMT = 6;               // rows per launch <= 192
-
-template <int MT>
-struct BigLds {
-  static constexpr int kX = MT * 32 * kXRow;      // one stage buffer
-  static constexpr int kPatch = kBigNW * 3 * 2048;  // per-wave patch buffers
-  static constexpr int kRed = 2 * MT * 4 * 1024;  // 2 waves x MT x 4 float4 x 64 lanes
-  static constexpr int kBytes = 2 * kX + kPatch + kRed;
-};
 
 // Position in a slice: unit (tile, record) and stage.
 struct StageIt {
@@ -869,126 +860,109 @@ struct StageIt {
   }
 };
 
-// Loads of one stage for one wave.
-struct BigSlot {
-  uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
-  u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
-  u32x2 lo[2];         // their low nibbles
-  uint32_t e[2][2];    // escape entries number lane and lane + 64 of the block
+// Weight loads run 2 stages ahead of the arithmetic and escape offsets 3;
+// the ring has one slot per stage of a unit, so one trip of the unit loop has
+// compile-time slots and a tile can only end between trips.
+constexpr int kBigDepth = kStages - 2;
+
+constexpr int kB8NW = 8;
+constexpr int kB8NT = kB8NW * 64;
+
+template <int MT>
+struct Big8Lds {
+  static constexpr int kRounds = (MT + 1) / 2;        // x pieces per thread per stage
+  static constexpr int kX = kRounds * 64 * kXRow;    // one stage buffer (64 rows per round)
+  static constexpr int kPatch = kB8NW * 2 * 2048;    // per wave: strip buffer + drop buffer
+  static constexpr int kRedMT = (MT + 1) / 2;        // M-tiles per reduction round
+  static constexpr int kRed = 4 * kRedMT * 4 * 1024; // 4 waves x kRedMT x 4 float4 x 64 lanes
+  static constexpr int kBytes = 2 * kX + kPatch + kRed;
 };
 
-// Per-stage loads of wave (cg, kg): subtile 2h + kg of strips 4p + 2cg + q.
-struct BigLoads {
+struct Big8Slot {
+  uint32_t off[2];  // esc_off of the escape block and of the next one
+  u32x4 hi;         // 8-bit view: 16 weights of channel lane%32, k half lane/32
+  u32x2 lo;         // their low nibbles
+  uint32_t e[2];    // escape entries number lane and lane + 64 of the block
+};
+
+// Per-stage loads of wave (s, kg): subtile 2h + kg of strip 4p + s.
+struct Big8Loads {
   const GemmParams& a;
-  int u0, u1, cg, kg, RK, S;
+  int u0, u1, s, kg, RK, S;
   uint32_t strip_bytes, v_hi, v_lo;
   rsrc_t r_esc;
 
-  __device__ __forceinline__ void issue_off(BigSlot& s, const StageIt& it) const {
-    const bool live = it.u < u1;
-    const int t = 2 * it.h + kg;
+  __device__ __forceinline__ void issue_off(Big8Slot& sl, const StageIt& it) const {
+    const int sq = 4 * it.p + s;
+    const bool ok = it.u < u1 && sq < S;
+    const uint32_t b = ok ? ((uint32_t)sq * RK + it.r) * 8 + 2 * it.h + kg : 0u;
     const cu32p c = scalar_view(a.w.esc_off);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int sq = 4 * it.p + 2 * cg + q;
-      const bool ok = live && sq < S;
-      const uint32_t b = ok ? ((uint32_t)sq * RK + it.r) * 8 + t : 0u;
-      const uint32_t o0 = c[b], o1 = c[b + 1];
-      s.off[q][0] = ok ? o0 : 0u;
-      s.off[q][1] = ok ? o1 : 0u;
-    }
+    const uint32_t o0 = c[b], o1 = c[b + 1];
+    sl.off[0] = ok ? o0 : 0u;
+    sl.off[1] = ok ? o1 : 0u;
   }
-  __device__ __forceinline__ void issue_w(BigSlot& s, const StageIt& it) const {
-    const bool live = it.u < u1;
+  __device__ __forceinline__ void issue_w(Big8Slot& sl, const StageIt& it) const {
+    const int sq = 4 * it.p + s;
+    const bool ok = it.u < u1 && sq < S;
     const uint32_t t = 2 * it.h + kg, so = (uint32_t)it.r * kRecBytes;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int sq = 4 * it.p + 2 * cg + q;
-      const bool ok = live && sq < S;
-      const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
-      s.hi[q] = bload4<kNonTemporal>(r, v_hi, so + t * 1024);
-      s.lo[q] = bload2<kNonTemporal>(r, v_lo, so + t * 512);
-    }
+    const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
+    sl.hi = bload4<kNonTemporal>(r, v_hi, so + t * 1024);
+    sl.lo = bload2<kNonTemporal>(r, v_lo, so + t * 512);
   }
-  __device__ __forceinline__ void issue_e(BigSlot& s, int lane) const {
+  __device__ __forceinline__ void issue_e(Big8Slot& sl, int lane) const {
+    const uint32_t o = sl.off[0];
+    const int c = (int)(sl.off[1] - o);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t o = s.off[q][0];
-      const int c = (int)(s.off[q][1] - o);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        s.e[q][h] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane + 64 * h, c - 1) : 0u) * 4u, 0);
-    }
+    for (int h = 0; h < 2; ++h)
+      sl.e[h] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane + 64 * h, c - 1) : 0u) * 4u, 0);
   }
 };
 
-// Per-wave patch region: two 2 KB strip buffers, then 2 KB where the stores of
-// a block without entries land, so the patch has no branch.
-constexpr int kBigPatchStride = 3 * 2048;
-
-// Restore of the lane's 2 x 16 weights of a stage and the escape patch for
-// the first 128 entries of each block, without a branch: every lane stores
-// one entry per 64 (lanes past the count hold the last entry again and
-// rewrite its slot with the same value), and the stores of an empty block go
-// to the drop buffer. Blocks with more entries finish in restore_big_rest.
-__device__ __forceinline__ void restore_big(const BigSlot& s, uint32_t bias0, uint32_t bias1, int cnt0, int cnt1,
-                                            char* patch, uint32_t plo, uint32_t (&P)[2][8]) {
-  decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y}, bias0, P[0]);
-  decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y}, bias1, P[1]);
-  patch_store(patch, plo, P[0]);
-  patch_store(patch + 2048, plo, P[1]);
+// Restore of one strip's 16 weights of the lane and the escape patch (first
+// 128 entries branch-free, as in restore_big; the rest in a second pass).
+__device__ __forceinline__ void restore_big8(const Big8Slot& sl, uint32_t bias, int cnt, char* patch, uint32_t plo,
+                                             int lane, rsrc_t r_esc, uint32_t (&P)[8]) {
+  decode16(uint4{sl.hi.x, sl.hi.y, sl.hi.z, sl.hi.w}, uint2{sl.lo.x, sl.lo.y}, bias, P);
+  patch_store(patch, plo, P);
   wave_lds_order();
-  const uint32_t base[2] = {cnt0 > 0 ? 0u : 4096u, cnt1 > 0 ? 2048u : 4096u};
+  const uint32_t base = cnt > 0 ? 0u : 2048u;
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t e = s.e[q][h];
-      const uint32_t at = base[q] + (((e << 6) & 0x600u) | ((e >> 1) & 0x1F0u) | ((e << 1) & 0xEu));
-      *reinterpret_cast<uint16_t*>(patch + at) = esc_bits(e);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t e = sl.e[h];
+    const uint32_t at = base + (((e << 6) & 0x600u) | ((e >> 1) & 0x1F0u) | ((e << 1) & 0xEu));
+    *reinterpret_cast<uint16_t*>(patch + at) = esc_bits(e);
+  }
   wave_lds_order();
-  patch_load(patch, plo, P[0]);
-  patch_load(patch + 2048, plo, P[1]);
-}
-// Entries 128 and on of blocks that have them (rare): a second patch pass.
-__device__ __forceinline__ void restore_big_rest(const BigSlot& s, int cnt0, int cnt1, char* patch, uint32_t plo,
-                                                 int lane, rsrc_t r_esc, uint32_t (&P)[2][8]) {
-  if (max(cnt0, cnt1) > 128) {
+  patch_load(patch, plo, P);
+  if (cnt > 128) {  // rare: the rest of the entries in a second pass
     wave_lds_order();
-    patch_store(patch, plo, P[0]);
-    patch_store(patch + 2048, plo, P[1]);
+    patch_store(patch, plo, P);
     wave_lds_order();
-    const int cq[2] = {cnt0, cnt1};
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t o = s.off[q][0];
-      for (int j = 128 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
-    }
+    const uint32_t o = sl.off[0];
+    for (int j = 128 + lane; j < cnt; j += 64) patch_put(patch, bload1(r_esc, (o + j) * 4u, 0));
     wave_lds_order();
-    patch_load(patch, plo, P[0]);
-    patch_load(patch + 2048, plo, P[1]);
+    patch_load(patch, plo, P);
   }
 }
 
-// Stage walk. The ring has one slot per stage of a unit, so one trip of the
-// loop is one unit with compile-time slots, and a tile can only end between
-// trips. Weight loads run 2 stages ahead, escape offsets 3; x of stage s + 1
-// is loaded at the start of stage s (before the weight loads, so waiting for
-// it never waits for them) and stored to LDS at its end; one barrier per
-// stage.
-constexpr int kBigDepth = kStages - 2;
-
+// Stage walk of the 8-wave layout. x runs two stages ahead in two register
+// sets (x of stage s + 2 is loaded at the start of stage s, stored at the end
+// of stage s + 1): loads complete in issue order, so the store's wait covers
+// the weight loads issued before it, and a second stage of lead time keeps
+// that wait from pacing the stages.
 template <int MT, typename XL, typename XS, typename TF, typename StepF>
-__device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, int u1, int RK, XL&& xload,
-                                         XS&& xstore, TF&& tile_end, StepF&& step) {
-  BigSlot ring[kStages];
+__device__ __forceinline__ void walk_big8(const Big8Loads& L, int lane, int u0, int u1, int RK, XL&& xload,
+                                          XS&& xstore, TF&& tile_end, StepF&& step) {
+  constexpr int XR = Big8Lds<MT>::kRounds;
+  Big8Slot ring[kStages];
   StageIt itO, itW, itX;
   itO.init(u0, RK);
   itW.init(u0, RK);
   itX.init(u0, RK);
-  u32x4 xr[MT];
-  xload(xr, itX);
+  u32x4 xr[2][XR];
+  xload(xr[0], itX);
+  itX.next(RK);
+  xload(xr[1], itX);
   itX.next(RK);
   L.issue_off(ring[0], itO);
   itO.next(RK);
@@ -1000,21 +974,21 @@ __device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, in
     L.issue_e(ring[j], lane);
     itW.next(RK);
   });
-  xstore(xr, 0);
+  xstore(xr[0], 0);
   lds_barrier();
   auto iteration = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    xload(xr, itX);
+    xload(xr[k & 1], itX);  // x of stage k + 2
     itX.next(RK);
     L.issue_off(ring[(k + kBigDepth + 1) % kStages], itO);
     itO.next(RK);
     L.issue_w(ring[(k + kBigDepth) % kStages], itW);
     L.issue_e(ring[(k + kBigDepth) % kStages], lane);
     itW.next(RK);
-    step(ring[k], k & 1, xr);
+    step(ring[k], k & 1);
+    xstore(xr[(k + 1) & 1], (k + 1) & 1);  // x of stage k + 1
     lds_barrier();
   };
-  // tile by tile: the inner loop carries the accumulators through MFMAs only
   for (int u = u0; u < u1;) {
     const int p = u / RK, ue = min(u1, (p + 1) * RK);
     for (; u < ue; ++u) static_for<kStages>(iteration);
@@ -1023,112 +997,82 @@ __device__ __forceinline__ void walk_big(const BigLoads& L, int lane, int u0, in
 }
 
 template <int MT, int EPI>
-__global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
-  using Lds = BigLds<MT>;
+__global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
+  using Lds = Big8Lds<MT>;
+  constexpr int XR = Lds::kRounds;
   __shared__ __align__(16) char lds[Lds::kBytes];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cg = wave & 1, kg = wave >> 1;
+  const int sw = wave & 3, kg = wave >> 2;
   const int g = logical_wg(blockIdx.x, a.G);
   const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
-  char* patch = lds + 2 * Lds::kX + wave * kBigPatchStride;
+  char* patch = lds + 2 * Lds::kX + wave * 4096;
   float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
 
-  f32x16 acc[2][MT];
+  f32x16 acc[MT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
-  const BigLoads L{a, u0, u1, cg, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
-                   (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
+  const Big8Loads L{a, u0, u1, sw, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
+                    (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t plo = patch_lane_off(lane);
 
-  // x staging: thread piece j = tid & 7 (16 B) of row 32 i + (tid >> 3)
+  // x staging: thread piece j = tid & 7 (16 B) of row 64 i + (tid >> 3)
   const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
-  const uint32_t row32 = 64u * (uint32_t)a.K;  // bytes of 32 rows
+  const uint32_t row64 = 128u * (uint32_t)a.K;  // bytes of 64 rows
   const uint32_t v_x = (uint32_t)(tid >> 3) * 2u * (uint32_t)a.K + (uint32_t)(tid & 7) * 16u;
   const uint32_t x_w = (uint32_t)(tid >> 3) * kXRow + (uint32_t)(tid & 7) * 16u;
-  auto xload = [&](u32x4 (&xr)[MT], const StageIt& it) __attribute__((always_inline)) {
+  auto xload = [&](u32x4 (&xr)[XR], const StageIt& it) __attribute__((always_inline)) {
     const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
     const uint32_t so = ((uint32_t)it.r * kRecK + (uint32_t)it.h * kStageK) * 2u;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) xr[i] = bload4(rx, v_x + i * row32, so);
+    for (int i = 0; i < XR; ++i) xr[i] = bload4(rx, v_x + i * row64, so);
   };
-  auto xstore = [&](const u32x4 (&xr)[MT], int buf) __attribute__((always_inline)) {
+  auto xstore = [&](const u32x4 (&xr)[XR], int buf) __attribute__((always_inline)) {
     char* b = lds + buf * Lds::kX + x_w;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) *reinterpret_cast<u32x4*>(b + i * 32 * kXRow) = xr[i];
+    for (int i = 0; i < XR; ++i) *reinterpret_cast<u32x4*>(b + i * 64 * kXRow) = xr[i];
   };
   // B fragment of (mt, i2): x[mt*32 + lane%32][32 kg + 16 (lane/32) + 8 i2 ..]
   const uint32_t x_r = (uint32_t)(lane & 31) * kXRow + 64u * kg + 32u * (uint32_t)(lane >> 5);
 
-  // MFMA operands of the previous stage: its products are issued during the
-  // next stage, interleaved with that stage's loads and restore. Zero
-  // operands (tile start) add exact zeros.
-  uint32_t Pp[2][8];
-  bf16x8 Bp[2][MT];
-  auto clear_pending = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Pp[q][i] = 0u;
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) Bp[i2][mt] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  };
-  auto mfma_pending = [&]() __attribute__((always_inline)) {
-    static_for<2>([&](auto ic) {
-      constexpr int i2 = decltype(ic)::value;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{Pp[0][4 * i2], Pp[0][4 * i2 + 1], Pp[0][4 * i2 + 2], Pp[0][4 * i2 + 3]});
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{Pp[1][4 * i2], Pp[1][4 * i2 + 1], Pp[1][4 * i2 + 2], Pp[1][4 * i2 + 3]});
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, Bp[i2][mt], acc[0][mt], 0, 0, 0);
-        acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, Bp[i2][mt], acc[1][mt], 0, 0, 0);
-      }
-    });
-  };
-  clear_pending();
-
-  // ---- tile end: last products, sum the two k halves, write or hand off
+  // ---- tile end: sum the two k halves of each strip, write or hand off
   auto flush = [&](int p) __attribute__((always_inline)) {
-    mfma_pending();
-    clear_pending();
     const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
+    const int c0 = sw * kStrip + 4 * (lane >> 5);  // channel within the tile
+    const bool cvalid = p * kBigTC + c0 < a.N;
     unsigned long long best[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) best[mt] = 0;
-    static_for<2>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
+    static_for<(MT + Lds::kRedMT - 1) / Lds::kRedMT>([&](auto rc) {
+      constexpr int m0 = decltype(rc)::value * Lds::kRedMT;
+      constexpr int m1 = m0 + Lds::kRedMT < MT ? m0 + Lds::kRedMT : MT;
+      if (m0 > 0) lds_barrier();
       if (kg == 1) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = m0; mt < m1; ++mt)
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<float4*>(red + (((cg * MT + mt) * 4 + rb) * 64 + lane) * 4) =
-                make_float4(acc[q][mt][4 * rb], acc[q][mt][4 * rb + 1], acc[q][mt][4 * rb + 2],
-                            acc[q][mt][4 * rb + 3]);
+            *reinterpret_cast<float4*>(red + (((sw * Lds::kRedMT + mt - m0) * 4 + rb) * 64 + lane) * 4) =
+                make_float4(acc[mt][4 * rb], acc[mt][4 * rb + 1], acc[mt][4 * rb + 2], acc[mt][4 * rb + 3]);
       }
       lds_barrier();
       if (kg == 0) {
-        const int c0 = (2 * cg + q) * kStrip + 4 * (lane >> 5);  // channel within the tile
-        const bool cvalid = p * kBigTC + c0 < a.N;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = m0; mt < m1; ++mt) {
           const int m = mt * 32 + (lane & 31);
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) {
-            const float4 o = *reinterpret_cast<const float4*>(red + (((cg * MT + mt) * 4 + rb) * 64 + lane) * 4);
-            const float4 v = make_float4(acc[q][mt][4 * rb] + o.x, acc[q][mt][4 * rb + 1] + o.y,
-                                         acc[q][mt][4 * rb + 2] + o.z, acc[q][mt][4 * rb + 3] + o.w);
+            const float4 o =
+                *reinterpret_cast<const float4*>(red + (((sw * Lds::kRedMT + mt - m0) * 4 + rb) * 64 + lane) * 4);
+            const float4 v = make_float4(acc[mt][4 * rb] + o.x, acc[mt][4 * rb + 1] + o.y,
+                                         acc[mt][4 * rb + 2] + o.z, acc[mt][4 * rb + 3] + o.w);
             const int c = c0 + 8 * rb, n = p * kBigTC + c;
             if (!whole) {
               if (m < a.M && cvalid) store_partial<kBigTC>(a, slot, m, c, v);
@@ -1157,7 +1101,6 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
           }
         }
       }
-      if (q == 0) lds_barrier();
     });
     if constexpr (EPI == kEpiArgmax) {
       if (whole && kg == 0) {
@@ -1173,61 +1116,38 @@ __global__ __launch_bounds__(kBigNT) void gemm_big_kernel(GemmParams a) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
   };
 
   StageIt cur;
   cur.init(u0, RK);
-  uint32_t bias[2] = {0u, 0u};
-  auto step = [&](const BigSlot& s, int buf, const u32x4 (&xr)[MT]) __attribute__((always_inline)) {
-    // tile start: this slot carries the window tops (empty loads read 0)
-    const uint32_t nt = (cur.h == 0 && (cur.r == 0 || cur.u == u0)) ? 0xFFFFFFFFu : 0u;
-    const int sw = 4 * cur.p + 2 * cg;
-    bias[0] = (strip_bias2(a.w.e_top, sw, sw < S, lane) & nt) | (bias[0] & ~nt);
-    bias[1] = (strip_bias2(a.w.e_top, sw + 1, sw + 1 < S, lane) & nt) | (bias[1] & ~nt);
-    // strips past the last and units past the slice load empty offsets: 0 entries
-    const int cnt0 = __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0]));
-    const int cnt1 = __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0]));
-    // this stage's B fragments, then the previous stage's products while
-    // this stage restores
+  uint32_t bias = 0u;
+  auto step = [&](const Big8Slot& sl, int buf) __attribute__((always_inline)) {
+    const int sq = 4 * cur.p + sw;
+    if (cur.h == 0 && (cur.r == 0 || cur.u == u0)) bias = strip_bias2(a.w.e_top, sq, sq < S, lane);
+    const int cnt = __builtin_amdgcn_readfirstlane((int)(sl.off[1] - sl.off[0]));
     const char* xb = lds + buf * Lds::kX + x_r;
-    bf16x8 bq[2][MT];
+    bf16x8 bq[MT];
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
+    for (int mt = 0; mt < MT; ++mt) bq[mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 32 * kXRow);
+    uint32_t P[8];
+    restore_big8(sl, bias, cnt, patch, plo, lane, L.r_esc, P);
+    static_for<2>([&](auto ic) {
+      constexpr int i2 = decltype(ic)::value;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{P[4 * i2], P[4 * i2 + 1], P[4 * i2 + 2], P[4 * i2 + 3]});
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) bq[i2][mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 32 * kXRow + 16 * i2);
-    mfma_pending();
-    uint32_t P[2][8];
-    restore_big(s, bias[0], bias[1], cnt0, cnt1, patch, plo, P);
-    // one product per few restore instructions, so the matrix unit runs
-    // while the restore issues
-    static_for<4 * MT>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // DS
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (i2 == 1) bq[mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 32 * kXRow + 16);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[mt], acc[mt], 0, 0, 0);
+      }
     });
-    // x of the next stage last: its loads have had the whole stage
-    __builtin_amdgcn_sched_barrier(0);
-    xstore(xr, buf ^ 1);
-    restore_big_rest(s, cnt0, cnt1, patch, plo, lane, L.r_esc, P);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Pp[q][i] = P[q][i];
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) Bp[i2][mt] = bq[i2][mt];
     cur.next(RK);
   };
 
-  if (u0 < u1) walk_big<MT>(L, lane, u0, u1, RK, xload, xstore, flush, step);
-  finish_slice<EPI, kBigNT, kBigTC, 8>(a, tid, u0, u1, &s_last);
+  if (u0 < u1) walk_big8<MT>(L, lane, u0, u1, RK, xload, xstore, flush, step);
+  finish_slice<EPI, kB8NT, kBigTC, 4>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ x rearrangement
@@ -1262,7 +1182,7 @@ KernelSel select_kernel(int M) {
     switch ((M + 31) / 32) {
 #define W12_BIG(MT) \
   case MT:          \
-    return {reinterpret_cast<const void*>(&gemm_big_kernel<MT, EPI>), 0, kBigNT};
+    return {reinterpret_cast<const void*>(&gemm_big8_kernel<MT, EPI>), 0, kB8NT};
       W12_BIG(3) W12_BIG(4) W12_BIG(5) W12_BIG(6)
 #undef W12_BIG
       default:
