@@ -98,10 +98,11 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
-    ap.add_argument("--workload", choices=("block", "batched", "stack"), default="block",
+    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep"), default="block",
                     help="block: one 27B-class block + LM head at M=32 (the headline line); "
                          "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
-                         "and 2%% outliers; stack: 64 blocks in sequence at M=32")
+                         "and 2%% outliers; stack: 64 blocks in sequence at M=32; "
+                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 192")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -126,6 +127,8 @@ def main():
         return run_batched(args, w12, synth, torch, dev)
     if args.workload == "stack":
         return run_stack(args, w12, synth, torch, dev)
+    if args.workload == "sweep":
+        return run_sweep(args, w12, synth, torch, dev)
 
     mats, pack_gbps = build_block(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
@@ -345,6 +348,43 @@ def run_batched(args, w12, synth, torch, dev):
                              "frac": round(gbps / HBM_PEAK_GBPS, 4)},
                      "mfma_bf16": {"achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_sweep(args, w12, synth, torch, dev):
+    """Time flatness in rows: Wgate|Wup 34816x5120 (block weight recipe) at
+    M = 1 ... 192, over >= 1 GiB of distinct packed copies, bf16 out."""
+    rows = (1, 8, 16, 32, 48, 64, 96, 128, 192)
+    w = torch.cat([synth.weights_bf16(FFN, HIDDEN, seed=1_000_000 * 2 + j, device=dev) for j in (5, 6)], dim=0)
+    pw = w12.w12_pack(w, check=True)
+    del w
+    ncopy = max(2, -(-(1 << 30) // pw.nbytes()))
+    copies = [pw] + [clone_packed(w12, pw) for _ in range(ncopy - 1)]
+    ws = w12.workspace(max(w12.gemm_workspace_bytes(pw.n, pw.k, m) for m in rows), dev)
+    by_rows = {}
+    for m in rows:
+        x = synth.activations_bf16(m, HIDDEN, seed=1_000_000 * 2 + 505, device=dev)
+        y = torch.empty(m, pw.n, dtype=torch.bfloat16, device=dev)
+        call = lambda i, x=x, y=y: w12.w12_gemm(copies[i % ncopy], x, out=y, ws=ws)
+        for i in range(max(args.warmup, ncopy)):
+            call(i)
+        torch.cuda.synchronize()
+        us = min(time_events(call, max(8, args.steps)) for _ in range(3))
+        nbytes = gemm_bytes(pw, m, 2)
+        by_rows[m] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "TFLOPs": round(2.0 * m * pw.n * pw.k / (us * 1e-6) / 1e12, 1)}
+        log(f"m={m}: {by_rows[m]}")
+    v = by_rows[M_ROWS]["GBps"]
+    line = {
+        "metric": "W12 verify GEMM effective HBM GB/s vs rows (Wgate|Wup 34816x5120)",
+        "value": v, "unit": "GB/s", "n_gpus": 1, "steps": max(8, args.steps), "warmup": args.warmup,
+        "ms_per_step": round(by_rows[M_ROWS]["us"] / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Wgate|Wup 34816x5120 (1.07% escapes), bf16 out, >= 1 GiB of rotated copies; "
+                               "value is the M=32 point", "rows": list(rows)},
+        "by_rows": {str(m): r for m, r in by_rows.items()},
+        "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBPS, 2),
     }
     print(json.dumps(line), flush=True)
 

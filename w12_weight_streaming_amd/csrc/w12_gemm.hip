@@ -683,11 +683,15 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
 template <int MV, int EPI>
 __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
-  // x rows of MV <= 2 ride in the load ring; more rows are loaded at the start
-  // of the unit, in groups of 4.
-  constexpr int XQ = MV <= 2 ? MV : 0;
-  constexpr int XG = MV < 4 ? MV : 4;
+  // x of the wave's subtile rides in the load ring. Up to 2 rows, each lane
+  // carries the 32 bytes of every row it multiplies (lanes of a half-wave
+  // hold the same bytes). For more rows, the wave's block of x (MV rows x 64
+  // bytes) rides as one 16-byte piece per lane and goes through a private
+  // 1 KB LDS buffer, from which the half-waves read their rows as broadcasts.
+  constexpr bool kXLds = MV > 2;
+  constexpr int XQ = kXLds ? 1 : MV;
   __shared__ __align__(16) float lds[kLdsFloats];
+  __shared__ __align__(16) char xlds[kXLds ? kNW * 1024 : 16];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -708,18 +712,24 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
                         (uint32_t)(kHiBytes + wave * 512 + lane * 8),
                         make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0 (voffset past the range)
-  const rsrc_t r_x = make_rsrc(a.x, x_bytes);
   const uint32_t plo = patch_lane_off(lane);
   // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
   const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
 
+  // block piece of this lane: row lane / 4, bytes 16 (lane % 4) of the
+  // subtile's 64 (rows >= m read 0)
+  const uint32_t v_xp = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)(wave * kSubK) * 2u + (uint32_t)(lane & 3) * 16u;
+  char* xw = xlds + (kXLds ? wave * 1024 : 0);
   auto issue_x = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    if constexpr (XQ > 0) {
-      const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
+    const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
+    const uint32_t so_x = (uint32_t)it.r * 512;
+    if constexpr (kXLds) {
+      s.xv[0][0] = bload4(rx, v_xp, so_x);
+    } else {
 #pragma unroll
       for (int m = 0; m < XQ; ++m) {
-        const uint32_t vx = v_x + m * row_bytes, so_x = (uint32_t)it.r * 512;
+        const uint32_t vx = v_x + m * row_bytes;
         s.xv[m][0] = bload4(rx, vx, so_x);
         s.xv[m][1] = bload4(rx, vx + 16, so_x);
       }
@@ -784,27 +794,23 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     }
     uint32_t P[2][8];
     restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
-    if constexpr (XQ > 0) {
+    if constexpr (kXLds) {
+      wave_lds_order();  // the previous unit's reads of the buffer come first
+      *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
+      wave_lds_order();
+      const char* xr = xw + 32 * (lane >> 5);
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(xr + m * 64);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(xr + m * 64 + 16);
+        acc[0][m] = dot16(P[0], x0, x1, acc[0][m]);
+        acc[1][m] = dot16(P[1], x0, x1, acc[1][m]);
+      }
+    } else {
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
         acc[0][m] = dot16(P[0], s.xv[m][0], s.xv[m][1], acc[0][m]);
         acc[1][m] = dot16(P[1], s.xv[m][0], s.xv[m][1], acc[1][m]);
-      }
-    } else {
-#pragma unroll
-      for (int m0 = 0; m0 < MV; m0 += XG) {
-        u32x4 xl[XG][2];
-#pragma unroll
-        for (int i = 0; i < XG; ++i) {
-          const uint32_t vx = v_x + (m0 + i) * row_bytes, so_x = (uint32_t)cur.r * 512;
-          xl[i][0] = bload4(r_x, vx, so_x);
-          xl[i][1] = bload4(r_x, vx + 16, so_x);
-        }
-#pragma unroll
-        for (int i = 0; i < XG; ++i) {
-          acc[0][m0 + i] = dot16(P[0], xl[i][0], xl[i][1], acc[0][m0 + i]);
-          acc[1][m0 + i] = dot16(P[1], xl[i][0], xl[i][1], acc[1][m0 + i]);
-        }
       }
     }
     cur.next(RK);
