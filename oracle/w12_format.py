@@ -21,6 +21,8 @@ Readings taken where the pages are open (each also listed in the design doc):
       block, so each channel's entries appear in ascending k.
   R6  record = 32 channels x 256 k (8192 weights = 12 KB, the pages' record
       size), byte placement given by `positions` below.
+  R17 the Q pass ([S1] 4.3) reads the 8-bit view with the dropped bits at
+      their midpoint and still restores escaped weights from the list.
 
 This module shares no code with the HIP path.
 """
@@ -158,6 +160,11 @@ def decode(packed: dict, n: int, k: int) -> np.ndarray:
     m = ((hi8 & 7) << 4) | lo4
     out = ((s << 15) | ((o + e_top[:, None] - 15) << 7) | m).astype(np.uint16)
 
+    return apply_escapes(out, packed, n, k)
+
+
+def apply_escapes(out: np.ndarray, packed: dict, n: int, k: int) -> np.ndarray:
+    """Write every escape entry's exact bf16 bits over its slot (R5)."""
     esc_off = packed["esc_off"].astype(np.int64)
     esc = packed["esc"].astype(np.uint32)
     nb = num_blocks(n, k)
@@ -182,6 +189,21 @@ def eight_bit_view(packed: dict, n: int, k: int) -> np.ndarray:
     s, o = hi8 >> 7, (hi8 >> 3) & 15
     m = ((hi8 & 7) << 4) | 8
     return ((s << 15) | ((o + e_top[:, None] - 15) << 7) | m).astype(np.uint16)
+
+
+def qpass_weights(packed: dict, n: int, k: int) -> np.ndarray:
+    """The weights a Q pass multiplies with ([S1] 4.3; reading R17): every
+    in-window weight from the 8-bit view alone, its four dropped low mantissa
+    bits at their midpoint 0b1000; escaped weights restored exactly from the
+    escape list, as the format restores them ([S1] 4.1)."""
+    check_shape(n, k)
+    return apply_escapes(eight_bit_view(packed, n, k), packed, n, k)
+
+
+def qpass_bytes(n: int, k: int, n_esc: int) -> int:
+    """Bytes a Q pass reads of a matrix: the 8-bit view (first 2/3 of every
+    record) + e_top + esc_off + escape entries."""
+    return n * k + n + 4 * (num_blocks(n, k) + 1) + 4 * n_esc
 
 
 def packed_bytes(n: int, k: int, n_esc: int) -> int:

@@ -271,6 +271,48 @@ def test_eight_bit_view_is_within_midpoint_error():
     assert np.all(np.abs(v8 - v) <= np.ldexp(8.0 / 128.0, (e - 127).astype(np.int32)))
 
 
+def test_qpass_weights_equal_decode_with_midpoint_nibbles():
+    """Independent route to the Q-pass weights: overwrite the low-nibble
+    plane of the records with 0b1000 and run the exact decoder."""
+    rng = np.random.default_rng(12)
+    n, k = 64, 768
+    w = rand_bits(rng, n, k, 110, 125)
+    w[rng.random((n, k)) < 0.03] = 0                      # escapes
+    w[rng.random((n, k)) < 0.01] = 0x7F00 | (w[0, 0] & 0x7F)  # far outliers
+    p = F.pack(w)
+    q = {kk: v.copy() for kk, v in p.items()}
+    rec = q["records"].reshape(-1, F.REC_BYTES)
+    rec[:, F.HI_BYTES:] = 0x88
+    assert np.array_equal(F.qpass_weights(p, n, k), F.decode(q, n, k))
+
+
+def test_qpass_weights_escapes_exact_rest_within_midpoint_error():
+    rng = np.random.default_rng(13)
+    n, k = 32, 512
+    w = rand_bits(rng, n, k, 112, 126)
+    w[rng.random((n, k)) < 0.05] = 0
+    w[rng.random((n, k)) < 0.02] = 0x0005                  # denormals escape
+    p = F.pack(w)
+    wq = F.qpass_weights(p, n, k)
+    e = (w.astype(np.int64) >> 7) & 0xFF
+    top = p["e_top"].astype(np.int64)[:, None]
+    in_window = (e >= 1) & (e <= 254) & (e >= top - 15) & (e <= top)
+    assert np.array_equal(wq[~in_window], w[~in_window])
+    v, vq = f32_of_bf16(w).astype(np.float64), f32_of_bf16(wq).astype(np.float64)
+    bound = np.ldexp(8.0 / 128.0, (e - 127).astype(np.int32))
+    assert np.all(np.abs(vq - v)[in_window] <= bound[in_window])
+    # a weight whose low nibble is already the midpoint comes back exactly
+    mid = in_window & ((w & 15) == 8)
+    assert mid.any() and np.array_equal(wq[mid], w[mid])
+
+
+def test_qpass_bytes_are_two_thirds_of_the_records():
+    n, k, n_esc = 1024, 1024, 11000
+    full = F.packed_bytes(n, k, n_esc)
+    q = F.qpass_bytes(n, k, n_esc)
+    assert full - q == n * k // 2
+
+
 def test_synthetic_escape_rate_and_density():
     """Sanity against the pages ([S1] 4.1): Gaussian weights under per-channel
     windows escape rarely (the pages report 7.33e-5 on a real checkpoint) and
