@@ -137,7 +137,8 @@ w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
  * w12_gemm -- verify GEMM ([S1] 4.1): y[i, c] = sum_k x[i, k] * W[c, k] for
  * the m verify rows, streaming every W12 record from HBM once, restoring it
  * in registers, fp32 accumulation. Rows m < 16 use a VALU dot-product path,
- * m >= 16 bf16 MFMA. The reduction over k is split across workgroups in a
+ * m >= 16 bf16 MFMA (more than 192 rows run as several launches of at most
+ * 192 rows, each streaming W again). The reduction over k is split across workgroups in a
  * fixed order (stream-K), so results are bitwise reproducible.
  *   x   [m, k] bf16 row-major, 1 <= m <= 256.
  *   y   [m, n] row-major, fp32 (W12_Y_F32) or bf16 (W12_Y_BF16, the
@@ -160,6 +161,22 @@ w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t *by
 w12_status w12_head_argmax(const w12_matrix *head, const uint16_t *x, int64_t m,
                            int32_t *idx, float *maxval, void *ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * w12_gemm_qpass, w12_head_argmax_qpass -- the Q pass ([S1] 4.3): the same
+ * products read from the 8-bit view alone (the first 2/3 of every record),
+ * every dropped low mantissa nibble taken at its midpoint 0b1000; escaped
+ * weights are restored from the escape list as in the exact pass. Arguments,
+ * layouts, workspace (w12_gemm_workspace) and errors as w12_gemm and
+ * w12_head_argmax; results are bitwise reproducible but are not those of the
+ * exact pass.
+ */
+w12_status w12_gemm_qpass(const w12_matrix *w, const uint16_t *x, int64_t m,
+                          void *y, int ytype, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+w12_status w12_head_argmax_qpass(const w12_matrix *head, const uint16_t *x, int64_t m,
+                                 int32_t *idx, float *maxval, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /*
  * tree_accept -- greedy tree verification ([S1] 1.1, 4.3; [S3]).

@@ -299,6 +299,61 @@ def test_head_argmax_exact_ties(w12, m):
     assert np.array_equal(host(idx), expect)
 
 
+# ----------------------------------------------------------------------------- Q pass (8-bit view)
+
+@pytest.fixture(scope="module")
+def qpass_mat(w12):
+    n, k = 320, 1792
+    bits = synth.bits_u16(gen(n, k, 61, p_zero=0.03, p_outlier=0.02))
+    pw, _ = pack_gpu(w12, bits)
+    wq = F.qpass_weights(F.pack(bits), n, k)
+    return pw, bits, wq
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 32, 64, 100, 192])
+def test_qpass_gemm_within_tolerance(w12, qpass_mat, m):
+    """w12_gemm_qpass against the oracle GEMM on the Q-pass weights."""
+    pw, bits, wq = qpass_mat
+    say("qpass gemm m", m)
+    x = synth.activations_bf16(m, pw.k, 62 + m)
+    y = w12.w12_gemm(pw, x.to(DEV), qpass=True)
+    y_ref, bound = V.gemm_ref(synth.bits_u16(x), wq)
+    ok = V.within_tolerance(host(y), y_ref, bound)
+    assert ok.all(), f"{(~ok).sum()} outputs out of tolerance"
+
+
+def test_qpass_is_not_the_exact_pass(w12, qpass_mat):
+    """The Q pass changes results (the low nibbles matter), and no more than
+    the midpoint error allows: |y_q - y| <= sum_k |x| * 2^(e-127) / 16."""
+    pw, bits, wq = qpass_mat
+    m = 32
+    x = synth.activations_bf16(m, pw.k, 70)
+    yq = host(w12.w12_gemm(pw, x.to(DEV), qpass=True)).astype(np.float64)
+    ye = host(w12.w12_gemm(pw, x.to(DEV))).astype(np.float64)
+    assert (yq != ye).mean() > 0.9
+    e = ((bits.astype(np.int64) >> 7) & 0xFF).astype(np.int32)
+    unit = np.where(e > 0, np.ldexp(1.0 / 16.0, e - 127), 0.0)
+    xa = np.abs(V.bf16_to_f64(synth.bits_u16(x)))
+    lim = xa @ unit.T
+    yref, bound = V.gemm_ref(synth.bits_u16(x), bits)
+    assert np.all(np.abs(yq - ye) <= lim + 2 * V.gemm_tolerance(bound))
+
+
+@pytest.mark.parametrize("m", [1, 32, 100])
+def test_qpass_head_argmax(w12, m):
+    n, k = 8192, 1024
+    bits = synth.bits_u16(gen(n, k, 71, p_zero=0.01, p_outlier=0.001))
+    pw, _ = pack_gpu(w12, bits)
+    wq = F.qpass_weights(F.pack(bits), n, k)
+    x = synth.activations_bf16(m, k, 72 + m)
+    idx, mx = w12.w12_head_argmax(pw, x.to(DEV), qpass=True)
+    ref_idx, ref_max, cands = V.head_argmax(synth.bits_u16(x), wq)
+    near = check_argmax(host(idx), ref_idx, cands)
+    say("qpass head m", m, "near-ties", near)
+    y = host(w12.w12_gemm(pw, x.to(DEV), qpass=True))
+    assert np.array_equal(host(mx), y[np.arange(m), host(idx)])
+
+
 # ----------------------------------------------------------------------------- tree acceptance
 
 def run_tree(w12, node_off, parent, token, argmax):

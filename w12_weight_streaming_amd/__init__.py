@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "w12_gemm": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
             "w12_head_argmax_workspace": (ctypes.c_int, [i64, i64, i64, ctypes.POINTER(sz)]),
             "w12_head_argmax": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
+            "w12_gemm_qpass": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
+            "w12_head_argmax_qpass": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "tree_accept": (ctypes.c_int, [i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -75,7 +77,8 @@ def lib() -> ctypes.CDLL:
 def exported_symbols():
     return ["w12_strerror", "w12_abi_version", "w12_num_blocks", "w12_pack_plan", "w12_pack",
             "w12_decode", "w12_check", "w12_gemm_workspace", "w12_gemm",
-            "w12_head_argmax_workspace", "w12_head_argmax", "tree_accept"]
+            "w12_head_argmax_workspace", "w12_head_argmax", "w12_gemm_qpass",
+            "w12_head_argmax_qpass", "tree_accept"]
 
 
 def _ok(status: int, what: str):
@@ -199,8 +202,10 @@ def gemm_workspace_bytes(n: int, k: int, m: int) -> int:
 
 
 def w12_gemm(pw: PackedW12, x: torch.Tensor, out: torch.Tensor | None = None,
-             out_dtype=torch.float32, ws: torch.Tensor | None = None) -> torch.Tensor:
-    """y[m, n] = x[m, :] . W[n, :] with W streamed from W12 (fp32 accumulate)."""
+             out_dtype=torch.float32, ws: torch.Tensor | None = None,
+             qpass: bool = False) -> torch.Tensor:
+    """y[m, n] = x[m, :] . W[n, :] with W streamed from W12 (fp32 accumulate).
+    qpass=True runs w12_gemm_qpass (8-bit view, midpoint low nibbles)."""
     _need(x, torch.bfloat16, "x", 2)
     m, k = x.shape
     if k != pw.k:
@@ -215,14 +220,15 @@ def w12_gemm(pw: PackedW12, x: torch.Tensor, out: torch.Tensor | None = None,
     if ws is None:
         ws = workspace(need, x.device)
     d = pw.desc()
-    _ok(lib().w12_gemm(ctypes.byref(d), _ptr(x), m, _ptr(out), yt, _ptr(ws), ws.numel(),
-                       _stream(x.device)), "w12_gemm")
+    fn, name = (lib().w12_gemm_qpass, "w12_gemm_qpass") if qpass else (lib().w12_gemm, "w12_gemm")
+    _ok(fn(ctypes.byref(d), _ptr(x), m, _ptr(out), yt, _ptr(ws), ws.numel(), _stream(x.device)), name)
     return out
 
 
 def w12_head_argmax(pw: PackedW12, x: torch.Tensor, ws: torch.Tensor | None = None,
-                    with_max: bool = True):
-    """Greedy token per row: (idx int32 [m], max logit float32 [m] or None)."""
+                    with_max: bool = True, qpass: bool = False):
+    """Greedy token per row: (idx int32 [m], max logit float32 [m] or None).
+    qpass=True runs w12_head_argmax_qpass (8-bit view, midpoint low nibbles)."""
     _need(x, torch.bfloat16, "x", 2)
     m, k = x.shape
     if k != pw.k:
@@ -235,8 +241,10 @@ def w12_head_argmax(pw: PackedW12, x: torch.Tensor, ws: torch.Tensor | None = No
     if ws is None:
         ws = workspace(need.value, x.device, "head")
     d = pw.desc()
-    _ok(lib().w12_head_argmax(ctypes.byref(d), _ptr(x), m, _ptr(idx), _ptr(mx), _ptr(ws),
-                              ws.numel(), _stream(x.device)), "w12_head_argmax")
+    fn, name = ((lib().w12_head_argmax_qpass, "w12_head_argmax_qpass") if qpass
+                else (lib().w12_head_argmax, "w12_head_argmax"))
+    _ok(fn(ctypes.byref(d), _ptr(x), m, _ptr(idx), _ptr(mx), _ptr(ws), ws.numel(),
+           _stream(x.device)), name)
     return idx, mx
 
 

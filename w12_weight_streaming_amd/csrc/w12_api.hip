@@ -72,7 +72,7 @@ size_t gemm_ws_bytes(int64_t n, int64_t k, int64_t m, int cu) {
 
 w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
                     int32_t* idx, float* maxval, void* ws, size_t ws_bytes, hipStream_t s,
-                    int epi) {
+                    int epi, bool qpass) {
   const int cu = num_cu();
   if (cu <= 0) return W12_EHIP;
   if (!ws) return W12_EINVAL;
@@ -102,10 +102,25 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
     p.done = reinterpret_cast<uint32_t*>(base + pl.off_done);
     p.idx = idx ? idx + m0 : nullptr;
     p.maxval = maxval ? maxval + m0 : nullptr;
-    const w12_status r = st(w12::launch_gemm(p, epi, s));
+    const w12_status r = st(w12::launch_gemm(p, epi, qpass, s));
     if (r != W12_OK) return r;
   }
   return W12_OK;
+}
+
+w12_status gemm_entry(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
+                      void* ws, size_t ws_bytes, hipStream_t stream, bool qpass) {
+  if (!matrix_ok(w) || !x || !y || m < 1 || m > kMaxRows) return W12_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return W12_EINVAL;
+  if (ytype != W12_Y_F32 && ytype != W12_Y_BF16) return W12_EINVAL;
+  return run_gemm(w, x, m, y, ytype, nullptr, nullptr, ws, ws_bytes, stream, w12::kEpiY, qpass);
+}
+
+w12_status head_entry(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,
+                      float* maxval, void* ws, size_t ws_bytes, hipStream_t stream, bool qpass) {
+  if (!matrix_ok(head) || !x || !idx || m < 1 || m > kMaxRows) return W12_EINVAL;
+  if (!aligned(x, 16)) return W12_EINVAL;
+  return run_gemm(head, x, m, nullptr, 0, idx, maxval, ws, ws_bytes, stream, w12::kEpiArgmax, qpass);
 }
 
 }  // namespace
@@ -164,12 +179,15 @@ w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
   return W12_OK;
 }
 
+
 w12_status w12_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!matrix_ok(w) || !x || !y || m < 1 || m > kMaxRows) return W12_EINVAL;
-  if (!aligned(x, 16) || !aligned(y, 16)) return W12_EINVAL;
-  if (ytype != W12_Y_F32 && ytype != W12_Y_BF16) return W12_EINVAL;
-  return run_gemm(w, x, m, y, ytype, nullptr, nullptr, ws, ws_bytes, stream, w12::kEpiY);
+  return gemm_entry(w, x, m, y, ytype, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_gemm_qpass(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  return gemm_entry(w, x, m, y, ytype, ws, ws_bytes, stream, true);
 }
 
 w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
@@ -178,9 +196,12 @@ w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* by
 
 w12_status w12_head_argmax(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,
                            float* maxval, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!matrix_ok(head) || !x || !idx || m < 1 || m > kMaxRows) return W12_EINVAL;
-  if (!aligned(x, 16)) return W12_EINVAL;
-  return run_gemm(head, x, m, nullptr, 0, idx, maxval, ws, ws_bytes, stream, w12::kEpiArgmax);
+  return head_entry(head, x, m, idx, maxval, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_head_argmax_qpass(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,
+                                 float* maxval, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return head_entry(head, x, m, idx, maxval, ws, ws_bytes, stream, true);
 }
 
 w12_status tree_accept(int32_t num_trees, const int32_t* node_off, int32_t total_nodes,

@@ -444,7 +444,11 @@ struct Ring {
 // The per-unit loads shared by both kernels. Strips past the last (the
 // missing second strip of a final tile) and units past the slice load
 // nothing: their resources are empty.
-template <int XQ>
+// The Q pass (QP) reads only the 8-bit view of each record; the low nibbles
+// it does not load are taken at their midpoint 0b1000.
+constexpr uint32_t kMidNibbles = 0x88888888u;
+
+template <int XQ, bool QP = false>
 struct UnitLoads {
   const GemmParams& a;
   int u0, u1, wave, lane, RK, S;
@@ -477,7 +481,11 @@ struct UnitLoads {
       const bool ok = live && sq < S;
       const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
       s.hi[q] = bload4<kNonTemporal>(r, v_hi, so);
-      s.lo[q] = bload2<kNonTemporal>(r, v_lo, so);
+      if constexpr (QP) {
+        s.lo[q] = u32x2{kMidNibbles, kMidNibbles};
+      } else {
+        s.lo[q] = bload2<kNonTemporal>(r, v_lo, so);
+      }
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ>& s, const UnitIt& it) const {
@@ -533,7 +541,7 @@ __device__ __forceinline__ void walk_slice(const LoadsT& L, int u0, int u1, int 
 
 // ============================================================================ MFMA path (m >= 16)
 
-template <int MT, int EPI>
+template <int MT, int EPI, bool QP>
 __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   // x fragments for MT <= 2 tiles of 32 rows ride in the load ring; larger m
   // loads them at the start of the unit (they are L2-resident).
@@ -556,7 +564,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
+  const UnitLoads<XQ, QP> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
                         (uint32_t)(wave * 1024 + lane * 16),
                         (uint32_t)(kHiBytes + wave * 512 + lane * 8),
                         make_rsrc(a.w.esc, 0xFFFFFFFFu)};
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
 // ============================================================================ VALU path (m < 16)
 
-template <int MV, int EPI>
+template <int MV, int EPI, bool QP>
 __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // x of the wave's subtile rides in the load ring. Up to 2 rows, each lane
   // carries the 32 bytes of every row it multiplies (lanes of a half-wave
@@ -707,7 +715,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
-  const UnitLoads<XQ> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
+  const UnitLoads<XQ, QP> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
                         (uint32_t)(wave * 1024 + lane * 16),
                         (uint32_t)(kHiBytes + wave * 512 + lane * 8),
                         make_rsrc(a.w.esc, 0xFFFFFFFFu)};
@@ -892,6 +900,7 @@ struct Big8Slot {
 };
 
 // Per-stage loads of wave (s, kg): subtile 2h + kg of strip 4p + s.
+template <bool QP>
 struct Big8Loads {
   const GemmParams& a;
   int u0, u1, s, kg, RK, S;
@@ -913,7 +922,11 @@ struct Big8Loads {
     const uint32_t t = 2 * it.h + kg, so = (uint32_t)it.r * kRecBytes;
     const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
     sl.hi = bload4<kNonTemporal>(r, v_hi, so + t * 1024);
-    sl.lo = bload2<kNonTemporal>(r, v_lo, so + t * 512);
+    if constexpr (QP) {
+      sl.lo = u32x2{kMidNibbles, kMidNibbles};
+    } else {
+      sl.lo = bload2<kNonTemporal>(r, v_lo, so + t * 512);
+    }
   }
   __device__ __forceinline__ void issue_e(Big8Slot& sl, int lane) const {
     const uint32_t o = sl.off[0];
@@ -956,8 +969,8 @@ __device__ __forceinline__ void restore_big8(const Big8Slot& sl, uint32_t bias, 
 // of stage s + 1): loads complete in issue order, so the store's wait covers
 // the weight loads issued before it, and a second stage of lead time keeps
 // that wait from pacing the stages.
-template <int MT, typename XL, typename XS, typename TF, typename StepF>
-__device__ __forceinline__ void walk_big8(const Big8Loads& L, int lane, int u0, int u1, int RK, XL&& xload,
+template <int MT, typename LoadsT, typename XL, typename XS, typename TF, typename StepF>
+__device__ __forceinline__ void walk_big8(const LoadsT& L, int lane, int u0, int u1, int RK, XL&& xload,
                                           XS&& xstore, TF&& tile_end, StepF&& step) {
   constexpr int XR = Big8Lds<MT>::kRounds;
   Big8Slot ring[kStages];
@@ -1002,7 +1015,7 @@ __device__ __forceinline__ void walk_big8(const Big8Loads& L, int lane, int u0, 
   }
 }
 
-template <int MT, int EPI>
+template <int MT, int EPI, bool QP>
 __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   using Lds = Big8Lds<MT>;
   constexpr int XR = Lds::kRounds;
@@ -1024,7 +1037,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
-  const Big8Loads L{a, u0, u1, sw, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
+  const Big8Loads<QP> L{a, u0, u1, sw, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
                     (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
   const uint32_t plo = patch_lane_off(lane);
 
@@ -1182,13 +1195,13 @@ struct KernelSel {
   int threads;  // workgroup size
 };
 
-template <int EPI>
+template <int EPI, bool QP>
 KernelSel select_kernel(int M) {
   if (M > kSmallMaxRows) {
     switch ((M + 31) / 32) {
 #define W12_BIG(MT) \
   case MT:          \
-    return {reinterpret_cast<const void*>(&gemm_big8_kernel<MT, EPI>), 0, kB8NT};
+    return {reinterpret_cast<const void*>(&gemm_big8_kernel<MT, EPI, QP>), 0, kB8NT};
       W12_BIG(3) W12_BIG(4) W12_BIG(5) W12_BIG(6)
 #undef W12_BIG
       default:
@@ -1196,14 +1209,14 @@ KernelSel select_kernel(int M) {
     }
   }
   if (M >= 16) {
-    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI>), 1, kNT};
-    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI>), 2, kNT};
+    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP>), 1, kNT};
+    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP>), 2, kNT};
   }
   const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   switch (mv) {
 #define W12_VALU(MV) \
   case MV:           \
-    return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI>), 0, kNT};
+    return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI, QP>), 0, kNT};
     W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(16)
 #undef W12_VALU
     default:
@@ -1244,8 +1257,9 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   return pl;
 }
 
-hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s) {
-  const KernelSel k = epi == kEpiY ? select_kernel<kEpiY>(p.M) : select_kernel<kEpiArgmax>(p.M);
+hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s) {
+  const KernelSel k = qpass ? (epi == kEpiY ? select_kernel<kEpiY, true>(p.M) : select_kernel<kEpiArgmax, true>(p.M))
+                            : (epi == kEpiY ? select_kernel<kEpiY, false>(p.M) : select_kernel<kEpiArgmax, false>(p.M));
   if (!k.fn) return hipErrorInvalidValue;
   if (k.mt > 0) {
     const int64_t chunks = (int64_t)(p.K / 32) * k.mt * 128;

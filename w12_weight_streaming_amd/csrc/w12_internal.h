@@ -54,7 +54,9 @@ struct GemmPlan {
 // Plan of one launch (m <= kRowsPerLaunch).
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu);
 
-hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s);
+// qpass: read only the 8-bit view of the records (low nibbles at their
+// midpoint); escapes are restored as in the exact pass.
+hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s);
 
 hipError_t launch_pack_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top,
                             uint32_t* esc_off, hipStream_t s);
