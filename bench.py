@@ -98,11 +98,12 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
-    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep"), default="block",
+    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep", "qpass"), default="block",
                     help="block: one 27B-class block + LM head at M=32 (the headline line); "
                          "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
                          "and 2%% outliers; stack: 64 blocks in sequence at M=32; "
-                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 192")
+                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 192; "
+                         "qpass: the block step through the Q pass (8-bit view only)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +130,8 @@ def main():
         return run_stack(args, w12, synth, torch, dev)
     if args.workload == "sweep":
         return run_sweep(args, w12, synth, torch, dev)
+    if args.workload == "qpass":
+        return run_qpass(args, w12, synth, torch, dev)
 
     mats, pack_gbps = build_block(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
@@ -385,6 +388,63 @@ def run_sweep(args, w12, synth, torch, dev):
                                "value is the M=32 point", "rows": list(rows)},
         "by_rows": {str(m): r for m, r in by_rows.items()},
         "pct_of_hbm_peak": round(100.0 * v / HBM_PEAK_GBPS, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def qpass_bytes(pw, m: int, out_bytes_per_elem: int) -> int:
+    """What a Q pass reads and writes: the 8-bit view (2/3 of the records) +
+    e_top + esc_off + escape entries + x + y."""
+    return pw.nbytes() - pw.n * pw.k // 2 + 2 * m * pw.k + out_bytes_per_elem * m * pw.n
+
+
+def run_qpass(args, w12, synth, torch, dev):
+    """The block step at M=32 through the Q pass (QKV, O, UP, DOWN GEMMs and
+    the LM-head argmax, reading only the 8-bit view of every record), next to
+    the exact pass, with the head's top-1 agreement between the two."""
+    mats, _ = build_block(w12, synth, torch, dev)
+    order = ["QKV", "O", "UP", "DOWN"]
+    outs = {n: torch.empty(M_ROWS, mats[n][0].n, dtype=torch.bfloat16, device=dev) for n in order}
+    head_pw, head_x = mats["HEAD"]
+    ws = w12.workspace(max(w12.gemm_workspace_bytes(mats[n][0].n, mats[n][0].k, M_ROWS)
+                           for n in order + ["HEAD"]), dev)
+
+    def step(qp):
+        for n in order:
+            w12.w12_gemm(mats[n][0], mats[n][1], out=outs[n], ws=ws, qpass=qp)
+        return w12.w12_head_argmax(head_pw, head_x, ws=ws, with_max=False, qpass=qp)[0]
+
+    res = {}
+    for qp in (False, True):
+        for _ in range(args.warmup):
+            step(qp)
+        torch.cuda.synchronize()
+        res[qp] = min(time_events(lambda i, qp=qp: step(qp), args.steps) for _ in range(3))
+    idx_q = step(True).cpu()
+    idx_e = step(False).cpu()
+    agree = float((idx_q == idx_e).float().mean())
+    # top-1 agreement over more rows: 256 fresh activation rows on the head
+    xs = synth.activations_bf16(256, HIDDEN, seed=1_000_000 * 4 + 900, device=dev)
+    a1 = w12.w12_head_argmax(head_pw, xs, with_max=False, qpass=True)[0]
+    a2 = w12.w12_head_argmax(head_pw, xs, with_max=False)[0]
+    agree_256 = float((a1 == a2).float().mean())
+    qbytes = sum(qpass_bytes(mats[n][0], M_ROWS, 2) for n in order) + \
+        qpass_bytes(head_pw, M_ROWS, 0) + 4 * M_ROWS
+    ebytes = sum(gemm_bytes(mats[n][0], M_ROWS, 2) for n in order) + \
+        head_pw.nbytes() + 2 * M_ROWS * HIDDEN + 4 * M_ROWS
+    gbps = qbytes / (res[True] * 1e-6) / 1e9
+    line = {
+        "metric": "W12 Q-pass (8-bit view) verify step effective HBM GB/s at M=32 rows",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res[True] / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Q pass of one 27B-class block (QKV, O, UP, DOWN) + LM-head argmax at M=32",
+                   "rows": M_ROWS, "bytes_per_step": int(qbytes)},
+        "exact_ms_per_step": round(res[False] / 1000.0, 4),
+        "exact_GBps": round(ebytes / (res[False] * 1e-6) / 1e9, 1),
+        "speedup_vs_exact": round(res[False] / res[True], 3),
+        "head_top1_agreement_32_rows": agree, "head_top1_agreement_256_rows": agree_256,
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
     }
     print(json.dumps(line), flush=True)
 
