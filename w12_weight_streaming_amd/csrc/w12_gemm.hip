@@ -356,11 +356,10 @@ __device__ __forceinline__ void patch_put(char* buf, uint32_t e) {
 // patch buffer, the lanes holding entries overwrite their slots, the pairs are
 // read back. Only the wave itself touches its buffer.
 template <typename SlotT>
-__device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uint32_t bias1, bool has0,
-                                             bool has1, char* patch, uint32_t plo, int lane, rsrc_t r_esc,
-                                             uint32_t (&P)[2][8]) {
-  const int cnt0 = has0 ? __builtin_amdgcn_readfirstlane((int)(s.off[0][1] - s.off[0][0])) : 0;
-  const int cnt1 = has1 ? __builtin_amdgcn_readfirstlane((int)(s.off[1][1] - s.off[1][0])) : 0;
+__device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uint32_t bias1, char* patch,
+                                             uint32_t plo, int lane, rsrc_t r_esc, uint32_t (&P)[2][8]) {
+  const int cnt0 = max(__builtin_amdgcn_readfirstlane((int)(s.off[0].y - s.off[0].x)), 0);
+  const int cnt1 = max(__builtin_amdgcn_readfirstlane((int)(s.off[1].y - s.off[1].x)), 0);
   decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y}, bias0, P[0]);
   decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y}, bias1, P[1]);
   if (cnt0 + cnt1 > 0) {
@@ -372,7 +371,7 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uin
     for (int q = 0; q < 2; ++q) {
       if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
       if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
-        const uint32_t o = __builtin_amdgcn_readfirstlane(s.off[q][0]);
+        const uint32_t o = __builtin_amdgcn_readfirstlane(s.off[q].x);
         for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
       }
     }
@@ -399,104 +398,163 @@ __device__ __forceinline__ unsigned long long row16_max(unsigned long long v) {
   return max_dpp<0x140>(v);  // row_mirror
 }
 
-// Position in a workgroup's slice of units: tile and record.
-struct UnitIt {
-  int u, p, r;
-  __device__ __forceinline__ void init(int u0, int RK) {
-    u = u0;
-    p = u0 / RK;
-    r = u0 - p * RK;
-  }
-  __device__ __forceinline__ void next(int RK) {
-    ++u;
-    if (++r == RK) {
-      r = 0;
-      ++p;
-    }
-  }
+// Wave-uniform position of a load stream in the workgroup's slice: the unit
+// it loads next, the units left before its next event (tile or slice
+// boundary) and that unit's tile.
+struct StreamPos {
+  int u, left, p;
 };
 
 // One unit's loads for one wave (subtile t = wave of both strips of a tile).
 template <int XQ>
 struct Slot {
-  uint32_t off[2][2];  // per strip: esc_off of the escape block and of the next one
+  u32x2 off[2];        // per strip: esc_off of the escape block and of the next one (every lane)
   u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[2];         // their low nibbles
+  uint32_t et[2];      // window top of the lane's channel
   uint32_t e[2];       // escape entry number `lane` of the block (if any)
-  u32x4 xv[XQ > 0 ? XQ : 1][2];  // x operands that ride with the unit
+  u32x4 xv[XQ][2];     // x operands that ride with the unit
 };
 
 // Load ordering: vector loads of a wave return in issue order, so a wait for
 // one load is a wait for every older one. Per unit there are three groups:
-//   O  escape-block offsets           issued D + 1 units ahead
-//   W  records, window tops, x        issued D units ahead
-//   E  escape entries (address <- O)  issued D units ahead, after W
-// Issuing E(u + D) waits for O(u + D), sent one iteration earlier, which only
-// needs groups of units <= u + D - 1 to have arrived. So D units of weight
-// loads stay in flight during the arithmetic of a unit. The ring holds D + 2
-// slots: O runs one slot ahead of W/E, and one slot is being computed.
+//   O  escape-block offsets                 issued D + 1 units ahead
+//   W  records, window tops, x              issued D units ahead
+//   E  escape entries (address <- O)        issued D units ahead, after the
+//                                           arithmetic of the current unit
+// E(u + D) needs O(u + D), which went out before W(u + D - 1); the only older
+// loads are those of unit u, which the arithmetic of unit u has just waited
+// for. So D units of weight loads stay in flight during that arithmetic. The
+// ring holds D + 2 slots: O runs one slot ahead of W/E, and one slot is being
+// computed.
 template <int XQ>
 struct Ring {
   static constexpr int NS = kDepth + 2;
   Slot<XQ> s[NS];
 };
 
-// The per-unit loads shared by both kernels. Strips past the last (the
-// missing second strip of a final tile) and units past the slice load
-// nothing: their resources are empty.
 // The Q pass (QP) reads only the 8-bit view of each record; the low nibbles
 // it does not load are taken at their midpoint 0b1000.
 constexpr uint32_t kMidNibbles = 0x88888888u;
 
+// The per-unit loads shared by both small-m kernels, as two wave-uniform
+// streams. Everything that changes only at a tile (the strips' record
+// resources, window-top offsets, escape-offset resources) is set up at the
+// tile's first unit; per unit the streams only advance scalar offsets.
+//  * W stream (records, window tops, x). Past the slice its resources are
+//    empty: the loads return zeros and move no data. A missing second strip
+//    (odd strip count) has an empty record resource and reads the first
+//    strip's window tops, so it restores finite values; its channels are
+//    never stored.
+//  * O stream (escape-block offsets, read by every lane through a resource
+//    that covers esc_off exactly). A missing strip, or a tile past the last,
+//    reads through an empty resource: offsets 0, 0, no escapes.
+//  * E (escape entries): lane l reads entry o0 + l through a resource that
+//    covers the n_esc entries; lanes past the block's count are not used.
 template <int XQ, bool QP = false>
 struct UnitLoads {
   const GemmParams& a;
-  int u0, u1, wave, lane, RK, S;
-  uint32_t strip_bytes, v_hi, v_lo;
-  rsrc_t r_esc;
+  int wave, RK, S, u1;
+  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c;
+  rsrc_t r_esc, r_off, r_none;
+  rsrc_t r_et;
+  const void* x_base;
+  uint32_t x_bytes, x_tile, x_step;
+  // W stream
+  StreamPos w;
+  rsrc_t rq[2], rx;
+  uint32_t so, sx, sb[2];
+  // O stream
+  StreamPos o;
+  rsrc_t ro[2];
+  uint32_t oo;
 
-  // Each strip gets its own record resource (empty when the strip or the unit
-  // does not exist), so every offset that may fall outside lives inside a
-  // range the hardware checks; scalar loads of missing strips or units read
-  // block 0 and are replaced by zero offsets.
-  __device__ __forceinline__ void issue_off(Slot<XQ>& s, const UnitIt& it) const {
-    const bool live = it.u < u1;
-    const cu32p c = scalar_view(a.w.esc_off);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int sq = 2 * it.p + q;
-      const bool ok = live && sq < S;
-      const uint32_t b = ok ? ((uint32_t)sq * RK + it.r) * 8 + wave : 0u;
-      const uint32_t o0 = c[b], o1 = c[b + 1];
-      s.off[q][0] = ok ? o0 : 0u;
-      s.off[q][1] = ok ? o1 : 0u;
-    }
+  __device__ __forceinline__ UnitLoads(const GemmParams& a_, int wave_, int lane, int u0, int u1_,
+                                       const void* xb, uint32_t xbytes, uint32_t xtile, uint32_t xstep)
+      : a(a_), wave(wave_), RK(a_.RK), S(a_.S), u1(u1_), x_base(xb), x_bytes(xbytes), x_tile(xtile),
+        x_step(xstep) {
+    strip_bytes = (uint32_t)RK * kRecBytes;
+    v_hi = (uint32_t)(wave * 1024 + lane * 16);
+    v_lo = (uint32_t)(kHiBytes + wave * 512 + lane * 8);
+    v_l4 = (uint32_t)lane * 4u;
+    v_c = (uint32_t)(lane & 31);
+    // escape count = esc_off[nb]; entries past it read as zero
+    const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
+    r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
+    r_off = make_rsrc(a.w.esc_off, (uint32_t)(a.w.nb + 1) * 4u);
+    r_none = make_rsrc(a.w.esc_off, 0u);
+    r_et = make_rsrc(a.w.e_top, (uint32_t)a.w.n);
+    const int p = u0 / RK, r = u0 - p * RK;
+    w = StreamPos{u0, min(RK - r, u1 - u0), p};
+    w_tile(r);
+    o = StreamPos{u0, RK - r, p};
+    o_tile(r);
   }
-  __device__ __forceinline__ void issue_w(Slot<XQ>& s, const UnitIt& it) const {
-    const bool live = it.u < u1;
-    const uint32_t so = (uint32_t)it.r * kRecBytes;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int sq = 2 * it.p + q;
-      const bool ok = live && sq < S;
-      const rsrc_t r = make_rsrc(a.w.rec + (int64_t)(ok ? sq : 0) * strip_bytes, ok ? strip_bytes : 0u);
-      s.hi[q] = bload4<kNonTemporal>(r, v_hi, so);
-      if constexpr (QP) {
-        s.lo[q] = u32x2{kMidNibbles, kMidNibbles};
+
+  // The W stream enters tile w.p at record r.
+  __device__ __forceinline__ void w_tile(int r) {
+    const int sq = 2 * w.p;
+    const bool has1 = sq + 1 < S;
+    const uint8_t* base = a.w.rec + (int64_t)sq * strip_bytes;
+    rq[0] = make_rsrc(base, strip_bytes);
+    rq[1] = make_rsrc(base + strip_bytes, has1 ? strip_bytes : 0u);
+    rx = make_rsrc(x_base, x_bytes);
+    so = (uint32_t)r * kRecBytes;
+    sx = x_tile + (uint32_t)r * x_step;
+    sb[0] = (uint32_t)sq * kStrip;
+    sb[1] = has1 ? sb[0] + kStrip : sb[0];
+  }
+  __device__ __forceinline__ void w_next() {
+    ++w.u;
+    so += kRecBytes;
+    sx += x_step;
+    if (--w.left == 0) {
+      if (w.u >= u1) {  // past the slice
+        rq[0] = rq[1] = rx = r_none;
+        w.left = 1 << 30;
       } else {
-        s.lo[q] = bload2<kNonTemporal>(r, v_lo, so);
+        ++w.p;
+        w_tile(0);
+        w.left = min(RK, u1 - w.u);
       }
     }
   }
-  __device__ __forceinline__ void issue_e(Slot<XQ>& s, const UnitIt& it) const {
-    const int p = it.p;
-    const bool has[2] = {2 * p < S, 2 * p + 1 < S};
+  // The O stream enters tile o.p at record r: escape block (strip, r, wave).
+  __device__ __forceinline__ void o_tile(int r) {
+    const int sq = 2 * o.p;
+    ro[0] = sq < S ? r_off : r_none;
+    ro[1] = sq + 1 < S ? r_off : r_none;
+    oo = (uint32_t)(((sq * RK + r) * 8 + wave) * 4);
+  }
+  __device__ __forceinline__ void o_next() {
+    ++o.u;
+    oo += 8 * 4;
+    if (--o.left == 0) {
+      ++o.p;
+      o_tile(0);
+      o.left = RK;
+    }
+  }
+
+  __device__ __forceinline__ void issue_off(Slot<XQ>& s) const {
+    s.off[0] = bload2(ro[0], 0u, oo);
+    s.off[1] = bload2(ro[1], 0u, oo + (uint32_t)RK * 32u);
+  }
+  __device__ __forceinline__ void issue_w(Slot<XQ>& s) const {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t o = s.off[q][0];
-      const int c = has[q] ? (int)(s.off[q][1] - o) : 0;
-      s.e[q] = bload1(r_esc, (c > 0 ? o + (uint32_t)min(lane, c - 1) : 0u) * 4u, 0);
+      s.hi[q] = bload4<kNonTemporal>(rq[q], v_hi, so);
+      if constexpr (QP) {
+        s.lo[q] = u32x2{kMidNibbles, kMidNibbles};
+      } else {
+        s.lo[q] = bload2<kNonTemporal>(rq[q], v_lo, so);
+      }
+      s.et[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r_et, (int)v_c, (int)sb[q], 0);
     }
+  }
+  __device__ __forceinline__ void issue_e(Slot<XQ>& s) const {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) s.e[q] = bload1(r_esc, s.off[q].x * 4u + v_l4, 0);
   }
 };
 
@@ -505,32 +563,29 @@ struct UnitLoads {
 // assume fewer loads in flight and wait for the next units' loads as well),
 // and a guarded tail of fewer than NS units.
 template <int XQ, typename LoadsT, typename XF, typename StepF>
-__device__ __forceinline__ void walk_slice(const LoadsT& L, int u0, int u1, int RK, XF&& issue_x, StepF&& step) {
+__device__ __forceinline__ void walk_slice(LoadsT& L, int u0, int u1, XF&& issue_x, StepF&& step) {
   Ring<XQ> ring;
   constexpr int NS = Ring<XQ>::NS;
-  UnitIt itO, itW;
-  itO.init(u0, RK);
-  itW.init(u0, RK);
-  L.issue_off(ring.s[0], itO);
-  itO.next(RK);
+  static_for<kDepth + 1>([&](auto jc) {
+    L.issue_off(ring.s[decltype(jc)::value]);
+    L.o_next();
+  });
   static_for<kDepth>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    L.issue_off(ring.s[j + 1], itO);
-    itO.next(RK);
-    L.issue_w(ring.s[j], itW);
-    issue_x(ring.s[j], itW);
-    L.issue_e(ring.s[j], itW);
-    itW.next(RK);
+    L.issue_w(ring.s[j]);
+    issue_x(ring.s[j]);
+    L.w_next();
   });
+  static_for<kDepth>([&](auto jc) { L.issue_e(ring.s[decltype(jc)::value]); });
   auto iteration = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    L.issue_off(ring.s[(k + kDepth + 1) % NS], itO);
-    itO.next(RK);
-    L.issue_w(ring.s[(k + kDepth) % NS], itW);
-    issue_x(ring.s[(k + kDepth) % NS], itW);
-    L.issue_e(ring.s[(k + kDepth) % NS], itW);
-    itW.next(RK);
+    L.issue_off(ring.s[(k + kDepth + 1) % NS]);
+    L.o_next();
+    L.issue_w(ring.s[(k + kDepth) % NS]);
+    issue_x(ring.s[(k + kDepth) % NS]);
+    L.w_next();
     step(ring.s[k]);
+    L.issue_e(ring.s[(k + kDepth) % NS]);
   };
   int base = u0;
   for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
@@ -539,13 +594,22 @@ __device__ __forceinline__ void walk_slice(const LoadsT& L, int u0, int u1, int 
   });
 }
 
+// Compute-side position: the tile whose units are being accumulated and the
+// units left in it. flush(p) runs when the tile ends.
+struct TileCursor {
+  int p, left, u;
+};
+
+// (E_n - 15) << 7 in both 16-bit halves, from the window top E_n.
+__device__ __forceinline__ uint32_t bias2_of_top(uint32_t e) { return e * 0x00800080u - 0x07800780u; }
+
 // ============================================================================ MFMA path (m >= 16)
 
 template <int MT, int EPI, bool QP>
 __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
-  // x fragments for MT <= 2 tiles of 32 rows ride in the load ring; larger m
-  // loads them at the start of the unit (they are L2-resident).
-  constexpr int XQ = MT <= 2 ? MT : 0;
+  // x fragments of the MT tiles of 32 rows ride in the load ring.
+  static_assert(MT >= 1 && MT <= 2, "small-m kernel: at most 64 rows");
+  constexpr int XQ = MT;
   __shared__ __align__(16) float lds[kLdsFloats];
   __shared__ int s_last;
 
@@ -564,24 +628,18 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  const UnitLoads<XQ, QP> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
-                        (uint32_t)(wave * 1024 + lane * 16),
-                        (uint32_t)(kHiBytes + wave * 512 + lane * 8),
-                        make_rsrc(a.w.esc, 0xFFFFFFFFu)};
-  const uint32_t xf_bytes = (uint32_t)(MT * 32) * (uint32_t)a.K * 2u;
-  const rsrc_t r_xf = make_rsrc(a.xf, xf_bytes);
+  // x fragment (record r, subtile t, tile mt, half h) of the fragment buffer
+  // is at ((r * 8 + t) * MT + mt) * 2048 + h * 1024.
+  UnitLoads<XQ, QP> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
+                      (uint32_t)(wave * MT * 2048), (uint32_t)(MT * 8 * 2048));
   const uint32_t plo = patch_lane_off(lane);
   const uint32_t v_x = (uint32_t)lane * 16u;
 
-  auto issue_x = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    if constexpr (XQ > 0) {
-      const rsrc_t rx = make_rsrc(a.xf, it.u < u1 ? xf_bytes : 0u);
-      const uint32_t b = (uint32_t)it.r * 8 + wave;
+  auto issue_x = [&](Slot<XQ>& s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < XQ; ++mt) {
-        s.xv[mt][0] = bload4(rx, v_x, ((b * MT + mt) * 2 + 0) * 1024);
-        s.xv[mt][1] = bload4(rx, v_x, ((b * MT + mt) * 2 + 1) * 1024);
-      }
+    for (int mt = 0; mt < XQ; ++mt) {
+      s.xv[mt][0] = bload4(L.rx, v_x + (uint32_t)(mt * 2048), L.sx);
+      s.xv[mt][1] = bload4(L.rx, v_x + (uint32_t)(mt * 2048 + 1024), L.sx);
     }
   };
 
@@ -632,38 +690,18 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   };
 
   // ---- arithmetic of one unit
-  UnitIt cur;
-  cur.init(u0, RK);
-  int tile_open = cur.p;
-  uint32_t bias[2] = {0u, 0u};
+  TileCursor cur{u0 / RK, min(RK - (u0 - (u0 / RK) * RK), u1 - u0), u0};
   auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
-    if (cur.p != tile_open) {
-      flush(tile_open);
-      tile_open = cur.p;
+    if (cur.left == 0) {
+      flush(cur.p);
+      ++cur.p;
+      cur.left = min(RK, u1 - cur.u);
     }
-    const int p = cur.p;
-    const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
-    if (cur.r == 0 || cur.u == u0) {  // new tile: window tops of its strips
-      bias[0] = strip_bias2(a.w.e_top, 2 * p, has0, lane);
-      bias[1] = strip_bias2(a.w.e_top, 2 * p + 1, has1, lane);
-    }
+    --cur.left;
+    ++cur.u;
     uint32_t P[2][8];
-    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
-    u32x4 xl[MT][2];
-    if constexpr (XQ > 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        xl[mt][0] = s.xv[mt][0];
-        xl[mt][1] = s.xv[mt][1];
-      }
-    } else {
-      const uint32_t b = (uint32_t)cur.r * 8 + wave;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        xl[mt][0] = bload4(r_xf, v_x, ((b * MT + mt) * 2 + 0) * 1024);
-        xl[mt][1] = bload4(r_xf, v_x, ((b * MT + mt) * 2 + 1) * 1024);
-      }
-    }
+    restore_unit(s, bias2_of_top(s.et[0]), bias2_of_top(s.et[1]), patch, plo, lane, L.r_esc, P);
+    const u32x4 (&xl)[MT][2] = s.xv;
     const bf16x8 a00 = __builtin_bit_cast(bf16x8, u32x4{P[0][0], P[0][1], P[0][2], P[0][3]});
     const bf16x8 a01 = __builtin_bit_cast(bf16x8, u32x4{P[0][4], P[0][5], P[0][6], P[0][7]});
     const bf16x8 a10 = __builtin_bit_cast(bf16x8, u32x4{P[1][0], P[1][1], P[1][2], P[1][3]});
@@ -677,12 +715,11 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, b0, acc[1][mt], 0, 0, 0);
       acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, b1, acc[1][mt], 0, 0, 0);
     }
-    cur.next(RK);
   };
 
   if (u0 < u1) {
-    walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
-    flush(tile_open);
+    walk_slice<XQ>(L, u0, u1, issue_x, step);
+    flush(cur.p);
   }
   finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
@@ -715,11 +752,8 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
-  const UnitLoads<XQ, QP> L{a, u0, u1, wave, lane, RK, S, (uint32_t)RK * kRecBytes,
-                        (uint32_t)(wave * 1024 + lane * 16),
-                        (uint32_t)(kHiBytes + wave * 512 + lane * 8),
-                        make_rsrc(a.w.esc, 0xFFFFFFFFu)};
-  const uint32_t x_bytes = (uint32_t)a.M * (uint32_t)a.K * 2u;  // rows >= M read 0 (voffset past the range)
+  // x rows >= M read 0 (voffset past the range); a record's x starts 512 bytes on.
+  UnitLoads<XQ, QP> L(a, wave, lane, u0, u1, a.x, (uint32_t)a.M * (uint32_t)a.K * 2u, 0u, 512u);
   const uint32_t plo = patch_lane_off(lane);
   // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
   const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
@@ -729,17 +763,15 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // subtile's 64 (rows >= m read 0)
   const uint32_t v_xp = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)(wave * kSubK) * 2u + (uint32_t)(lane & 3) * 16u;
   char* xw = xlds + (kXLds ? wave * 1024 : 0);
-  auto issue_x = [&](Slot<XQ>& s, const UnitIt& it) __attribute__((always_inline)) {
-    const rsrc_t rx = make_rsrc(a.x, it.u < u1 ? x_bytes : 0u);
-    const uint32_t so_x = (uint32_t)it.r * 512;
+  auto issue_x = [&](Slot<XQ>& s) __attribute__((always_inline)) {
     if constexpr (kXLds) {
-      s.xv[0][0] = bload4(rx, v_xp, so_x);
+      s.xv[0][0] = bload4(L.rx, v_xp, L.sx);
     } else {
 #pragma unroll
       for (int m = 0; m < XQ; ++m) {
         const uint32_t vx = v_x + m * row_bytes;
-        s.xv[m][0] = bload4(rx, vx, so_x);
-        s.xv[m][1] = bload4(rx, vx + 16, so_x);
+        s.xv[m][0] = bload4(L.rx, vx, L.sx);
+        s.xv[m][1] = bload4(L.rx, vx + 16, L.sx);
       }
     }
   };
@@ -785,23 +817,17 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     return sum;
   };
 
-  UnitIt cur;
-  cur.init(u0, RK);
-  int tile_open = cur.p;
-  uint32_t bias[2] = {0u, 0u};
+  TileCursor cur{u0 / RK, min(RK - (u0 - (u0 / RK) * RK), u1 - u0), u0};
   auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
-    if (cur.p != tile_open) {
-      flush(tile_open);
-      tile_open = cur.p;
+    if (cur.left == 0) {
+      flush(cur.p);
+      ++cur.p;
+      cur.left = min(RK, u1 - cur.u);
     }
-    const int p = cur.p;
-    const bool has0 = 2 * p < S, has1 = 2 * p + 1 < S;
-    if (cur.r == 0 || cur.u == u0) {  // new tile: window tops of its strips
-      bias[0] = strip_bias2(a.w.e_top, 2 * p, has0, lane);
-      bias[1] = strip_bias2(a.w.e_top, 2 * p + 1, has1, lane);
-    }
+    --cur.left;
+    ++cur.u;
     uint32_t P[2][8];
-    restore_unit(s, bias[0], bias[1], has0, has1, patch, plo, lane, L.r_esc, P);
+    restore_unit(s, bias2_of_top(s.et[0]), bias2_of_top(s.et[1]), patch, plo, lane, L.r_esc, P);
     if constexpr (kXLds) {
       wave_lds_order();  // the previous unit's reads of the buffer come first
       *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
@@ -821,12 +847,11 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
         acc[1][m] = dot16(P[1], s.xv[m][0], s.xv[m][1], acc[1][m]);
       }
     }
-    cur.next(RK);
   };
 
   if (u0 < u1) {
-    walk_slice<XQ>(L, u0, u1, RK, issue_x, step);
-    flush(tile_open);
+    walk_slice<XQ>(L, u0, u1, issue_x, step);
+    flush(cur.p);
   }
   finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
