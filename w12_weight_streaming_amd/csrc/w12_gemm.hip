@@ -152,8 +152,33 @@ __device__ __forceinline__ int owner_of(int u, int U, int G) {
 
 __device__ __forceinline__ unsigned long long row16_max(unsigned long long v);
 
+// Argmax key of row m over channels n .. n+3 -- (value key, ~index), so the
+// maximum is the largest logit, lowest id on ties -- maximised over the 16
+// threads of the DPP row (which hold the row's 64 channels of a tile); 0 when
+// no channel is valid.
+__device__ __forceinline__ unsigned long long row_key4(const GemmParams& a, int m, int n, float4 v) {
+  unsigned long long best = 0;
+  if (m < a.M && n < a.N) {
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned long long key = ((unsigned long long)float_key(vv[i]) << 32) |
+                                     (uint32_t)(0xFFFFFFFFu - (uint32_t)(n + i));
+      best = key > best ? key : best;
+    }
+  }
+  return row16_max(best);
+}
+__device__ __forceinline__ unsigned long long kmax(unsigned long long x, unsigned long long y) { return x > y ? x : y; }
+
 // Final value of 4 consecutive channels (n .. n+3) of row m. For the argmax
 // epilogue, 16 consecutive threads of a wave hold one row's 64 channels.
+//
+// Whole tiles of the argmax epilogue do not come here: their keys are kept per
+// thread across the slice and published once at its end (publish_keys). On
+// this family a wave's stores and atomics count in the same in-order counter
+// as its loads, so a device-scope atomic at every tile end would hold up the
+// weight loads issued after it until the atomic completed.
 template <int EPI>
 __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n, float4 v) {
   const bool valid = m < a.M && n < a.N;
@@ -168,18 +193,7 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
           make_uint2(lo, hi);
     }
   } else {
-    // (value key, ~index): the max is the largest logit, lowest id on ties.
-    unsigned long long best = 0;
-    if (valid) {
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned long long key = ((unsigned long long)float_key(vv[i]) << 32) |
-                                       (uint32_t)(0xFFFFFFFFu - (uint32_t)(n + i));
-        best = key > best ? key : best;
-      }
-    }
-    best = row16_max(best);
+    const unsigned long long best = row_key4(a, m, n, v);
     if ((tid & 15) == 0 && best) atomicMax(&a.keys[m], best);
   }
 }
@@ -411,7 +425,7 @@ struct Slot {
   u32x2 off[2];        // per strip: esc_off of the escape block and of the next one (every lane)
   u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[2];         // their low nibbles
-  uint32_t et[2];      // window top of the lane's channel
+  uint32_t et[2];      // the 4 window tops around the lane's channel (its byte: lane % 4)
   uint32_t e[2];       // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ][2];     // x operands that ride with the unit
 };
@@ -455,7 +469,7 @@ template <int XQ, bool QP = false>
 struct UnitLoads {
   const GemmParams& a;
   int wave, RK, S, u1;
-  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c;
+  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4;
   rsrc_t r_esc, r_off, r_none;
   rsrc_t r_et;
   const void* x_base;
@@ -477,7 +491,7 @@ struct UnitLoads {
     v_hi = (uint32_t)(wave * 1024 + lane * 16);
     v_lo = (uint32_t)(kHiBytes + wave * 512 + lane * 8);
     v_l4 = (uint32_t)lane * 4u;
-    v_c = (uint32_t)(lane & 31);
+    v_c4 = (uint32_t)(lane & 28);
     // escape count = esc_off[nb]; entries past it read as zero
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
@@ -549,7 +563,9 @@ struct UnitLoads {
       } else {
         s.lo[q] = bload2<kNonTemporal>(rq[q], v_lo, so);
       }
-      s.et[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r_et, (int)v_c, (int)sb[q], 0);
+      // a whole dword: a byte load's result would be widened where the ring
+      // wraps round, which makes the compiler wait for the load right there
+      s.et[q] = bload1(r_et, v_c4, sb[q]);
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ>& s) const {
@@ -600,8 +616,11 @@ struct TileCursor {
   int p, left, u;
 };
 
-// (E_n - 15) << 7 in both 16-bit halves, from the window top E_n.
-__device__ __forceinline__ uint32_t bias2_of_top(uint32_t e) { return e * 0x00800080u - 0x07800780u; }
+// (E_n - 15) << 7 in both 16-bit halves, from the dword of window tops that
+// holds E_n in byte lane % 4.
+__device__ __forceinline__ uint32_t bias2_of_top(uint32_t et4, int lane) {
+  return __builtin_amdgcn_ubfe(et4, 8u * (uint32_t)(lane & 3), 8) * 0x00800080u - 0x07800780u;
+}
 
 // ============================================================================ MFMA path (m >= 16)
 
@@ -621,6 +640,9 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
 
   f32x16 acc[2][MT];
+  unsigned long long run[MT];  // argmax: best key of row mt * 32 + tid / 16 over the slice's whole tiles
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) run[mt] = 0;
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -675,7 +697,11 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
                                    *reinterpret_cast<const float4*>(b + 3 * kSlotFloats)));
       const int m = mt * 32 + ml;
       if (whole) {
-        emit4<EPI>(a, tid, m, p * 64 + c4, v);
+        if constexpr (EPI == kEpiArgmax) {
+          run[mt] = kmax(run[mt], row_key4(a, m, p * 64 + c4, v));
+        } else {
+          emit4<EPI>(a, tid, m, p * 64 + c4, v);
+        }
       } else if (m < a.M) {
         store_partial<64>(a, slot, m, c4, v);
       }
@@ -700,7 +726,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     --cur.left;
     ++cur.u;
     uint32_t P[2][8];
-    restore_unit(s, bias2_of_top(s.et[0]), bias2_of_top(s.et[1]), patch, plo, lane, L.r_esc, P);
+    restore_unit(s, bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane), patch, plo, lane, L.r_esc, P);
     const u32x4 (&xl)[MT][2] = s.xv;
     const bf16x8 a00 = __builtin_bit_cast(bf16x8, u32x4{P[0][0], P[0][1], P[0][2], P[0][3]});
     const bf16x8 a01 = __builtin_bit_cast(bf16x8, u32x4{P[0][4], P[0][5], P[0][6], P[0][7]});
@@ -720,6 +746,11 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   if (u0 < u1) {
     walk_slice<XQ>(L, u0, u1, issue_x, step);
     flush(cur.p);
+  }
+  if constexpr (EPI == kEpiArgmax) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      if ((tid & 15) == 0 && run[mt]) atomicMax(&a.keys[mt * 32 + (tid >> 4)], run[mt]);
   }
   finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
@@ -747,6 +778,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
 
   float acc[2][MV];
+  unsigned long long run = 0;  // argmax: best key of row tid / 16 over the slice's whole tiles
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -796,7 +828,11 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
       for (int w = 0; w < kNW; ++w)
         v = f4add(v, *reinterpret_cast<const float4*>(lds + ((w * 2 + q) * MV + m) * 32 + c));
       if (whole) {
-        emit4<EPI>(a, tid, m, p * 64 + c4, v);
+        if constexpr (EPI == kEpiArgmax) {
+          run = kmax(run, row_key4(a, m, p * 64 + c4, v));
+        } else {
+          emit4<EPI>(a, tid, m, p * 64 + c4, v);
+        }
       } else if (m < a.M) {
         store_partial<64>(a, slot, m, c4, v);
       }
@@ -827,7 +863,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     --cur.left;
     ++cur.u;
     uint32_t P[2][8];
-    restore_unit(s, bias2_of_top(s.et[0]), bias2_of_top(s.et[1]), patch, plo, lane, L.r_esc, P);
+    restore_unit(s, bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane), patch, plo, lane, L.r_esc, P);
     if constexpr (kXLds) {
       wave_lds_order();  // the previous unit's reads of the buffer come first
       *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
@@ -852,6 +888,9 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   if (u0 < u1) {
     walk_slice<XQ>(L, u0, u1, issue_x, step);
     flush(cur.p);
+  }
+  if constexpr (EPI == kEpiArgmax) {
+    if ((tid & 15) == 0 && tid < MV * 16 && run) atomicMax(&a.keys[tid >> 4], run);
   }
   finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
@@ -1057,6 +1096,11 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
 
   f32x16 acc[MT];
+  // argmax: lanes < 32 of the kg = 0 waves keep the best key of row
+  // mt * 32 + lane over their strip of the slice's whole tiles
+  unsigned long long run[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) run[mt] = 0;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1154,8 +1198,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
           const uint32_t lo = (uint32_t)best[mt], hi = (uint32_t)(best[mt] >> 32);
           const unsigned long long o = ((unsigned long long)(uint32_t)__shfl_xor((int)hi, 32, 64) << 32) |
                                        (uint32_t)__shfl_xor((int)lo, 32, 64);
-          const unsigned long long b = o > best[mt] ? o : best[mt];
-          if (lane < 32 && m < a.M && b) atomicMax(&a.keys[m], b);
+          if (lane < 32 && m < a.M) run[mt] = kmax(run[mt], kmax(o, best[mt]));
         }
       }
     }
@@ -1191,6 +1234,11 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   };
 
   if (u0 < u1) walk_big8<MT>(L, lane, u0, u1, RK, xload, xstore, flush, step);
+  if constexpr (EPI == kEpiArgmax) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      if (run[mt]) atomicMax(&a.keys[mt * 32 + (lane & 31)], run[mt]);
+  }
   finish_slice<EPI, kB8NT, kBigTC, 4>(a, tid, u0, u1, &s_last);
 }
 
