@@ -50,6 +50,7 @@ constexpr int kNT = kNW * 64;
 constexpr int kRedStride = 68;                  // floats per 64-channel row (+4 pad)
 constexpr int kSlotFloats = 32 * kRedStride;    // one 32-row x 64-channel reduction slot
 constexpr int kLdsFloats = 4 * kSlotFloats;     // 34816 B >= 8 waves x 4 KB of patch buffers
+constexpr int kMfmaLdsFloats = kNW * kSlotFloats;  // one reduction slot per wave (aliases the patch buffers)
 constexpr int kRawBufferWord3 = 0x00020000;     // gfx9-family raw buffer descriptor word 3
 constexpr int kNonTemporal = 2;                 // load cache policy: streaming
 
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   // x fragments of the MT tiles of 32 rows ride in the load ring.
   static_assert(MT >= 1 && MT <= 2, "small-m kernel: at most 64 rows");
   constexpr int XQ = MT;
-  __shared__ __align__(16) float lds[kLdsFloats];
+  __shared__ __align__(16) float lds[kMfmaLdsFloats];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -665,36 +666,34 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     }
   };
 
-  // ---- tile end: reduce the 8 waves' accumulators, write or hand off
+  // ---- tile end: reduce the 8 waves' accumulators, write or hand off. Every
+  // wave writes its 32 x 64 partial to a slot of its own, then each thread
+  // sums one row quad over the 8 slots in a fixed order.
   auto flush = [&](int p) __attribute__((always_inline)) {
     const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
     static_for<MT>([&](auto mtc) {
       constexpr int mt = decltype(mtc)::value;
-      auto put = [&](float* dst, bool add) __attribute__((always_inline)) {
+      lds_barrier();  // the slots (and patch buffers) are free
+      {
+        float* dst = lds + wave * kSlotFloats;
         const int ml = lane & 31, hf = lane >> 5;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            float4* d = reinterpret_cast<float4*>(dst + ml * kRedStride + 32 * q + 8 * rb + 4 * hf);
-            float4 v = make_float4(acc[q][mt][4 * rb], acc[q][mt][4 * rb + 1],
-                                   acc[q][mt][4 * rb + 2], acc[q][mt][4 * rb + 3]);
-            if (add) v = f4add(*d, v);
-            *d = v;
-          }
-      };
-      lds_barrier();
-      if (wave >= 4) put(lds + (wave - 4) * kSlotFloats, false);
-      lds_barrier();
-      if (wave < 4) put(lds + wave * kSlotFloats, true);
+          for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4*>(dst + ml * kRedStride + 32 * q + 8 * rb + 4 * hf) =
+                make_float4(acc[q][mt][4 * rb], acc[q][mt][4 * rb + 1], acc[q][mt][4 * rb + 2],
+                            acc[q][mt][4 * rb + 3]);
+      }
       lds_barrier();
       const int ml = tid >> 4, c4 = (tid & 15) * 4;  // 32 rows x 16 channel quads = kNT
       const float* b = lds + ml * kRedStride + c4;
-      const float4 v = f4add(f4add(*reinterpret_cast<const float4*>(b),
-                                   *reinterpret_cast<const float4*>(b + kSlotFloats)),
-                             f4add(*reinterpret_cast<const float4*>(b + 2 * kSlotFloats),
-                                   *reinterpret_cast<const float4*>(b + 3 * kSlotFloats)));
+      float4 sw[kNW];
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) sw[w] = *reinterpret_cast<const float4*>(b + w * kSlotFloats);
+      const float4 v = f4add(f4add(f4add(sw[0], sw[4]), f4add(sw[1], sw[5])),
+                             f4add(f4add(sw[2], sw[6]), f4add(sw[3], sw[7])));
       const int m = mt * 32 + ml;
       if (whole) {
         if constexpr (EPI == kEpiArgmax) {
