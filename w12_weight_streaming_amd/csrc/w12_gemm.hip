@@ -50,7 +50,6 @@ constexpr int kNT = kNW * 64;
 constexpr int kRedStride = 68;                  // floats per 64-channel row (+4 pad)
 constexpr int kSlotFloats = 32 * kRedStride;    // one 32-row x 64-channel reduction slot
 constexpr int kLdsFloats = 4 * kSlotFloats;     // 34816 B >= 8 waves x 4 KB of patch buffers
-constexpr int kMfmaLdsFloats = kNW * kSlotFloats;  // one reduction slot per wave (aliases the patch buffers)
 constexpr int kRawBufferWord3 = 0x00020000;     // gfx9-family raw buffer descriptor word 3
 constexpr int kNonTemporal = 2;                 // load cache policy: streaming
 
@@ -366,24 +365,29 @@ __device__ __forceinline__ void patch_put(char* buf, uint32_t e) {
   *reinterpret_cast<uint16_t*>(buf + at) = esc_bits(e);
 }
 
-// Restore the lane's 2 x 16 weights of a unit (both strips of the tile) and
-// apply the escape blocks' entries: the restored pairs go to the wave's LDS
-// patch buffer, the lanes holding entries overwrite their slots, the pairs are
-// read back. Only the wave itself touches its buffer.
-template <typename SlotT>
-__device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uint32_t bias1, char* patch,
-                                             uint32_t plo, int lane, rsrc_t r_esc, uint32_t (&P)[2][8]) {
-  const int cnt0 = max(__builtin_amdgcn_readfirstlane((int)(s.off[0].y - s.off[0].x)), 0);
-  const int cnt1 = max(__builtin_amdgcn_readfirstlane((int)(s.off[1].y - s.off[1].x)), 0);
-  decode16(uint4{s.hi[0].x, s.hi[0].y, s.hi[0].z, s.hi[0].w}, uint2{s.lo[0].x, s.lo[0].y}, bias0, P[0]);
-  decode16(uint4{s.hi[1].x, s.hi[1].y, s.hi[1].z, s.hi[1].w}, uint2{s.lo[1].x, s.lo[1].y}, bias1, P[1]);
-  if (cnt0 + cnt1 > 0) {
-    patch_store(patch, plo, P[0]);
-    patch_store(patch + 2048, plo, P[1]);
-    wave_lds_order();
-    const int cq[2] = {cnt0, cnt1};
+// Restore the lane's NQ x 16 weights of a unit (one subtile of each strip of
+// the tile) and apply the escape blocks' entries: the restored pairs go to the
+// wave's LDS patch buffer (2 KB per strip), the lanes holding entries overwrite
+// their slots, the pairs are read back. Only the wave itself touches its buffer.
+template <int NQ, typename SlotT>
+__device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bias)[NQ], char* patch,
+                                             uint32_t plo, int lane, rsrc_t r_esc, uint32_t (&P)[NQ][8]) {
+  int cq[NQ];
+  int any = 0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < NQ; ++q) {
+    cq[q] = max(__builtin_amdgcn_readfirstlane((int)(s.off[q].y - s.off[q].x)), 0);
+    any |= cq[q];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+    decode16(uint4{s.hi[q].x, s.hi[q].y, s.hi[q].z, s.hi[q].w}, uint2{s.lo[q].x, s.lo[q].y}, bias[q], P[q]);
+  if (any > 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) patch_store(patch + q * 2048, plo, P[q]);
+    wave_lds_order();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
       if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
       if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
         const uint32_t o = __builtin_amdgcn_readfirstlane(s.off[q].x);
@@ -391,8 +395,8 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, uint32_t bias0, uin
       }
     }
     wave_lds_order();
-    patch_load(patch, plo, P[0]);
-    patch_load(patch + 2048, plo, P[1]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) patch_load(patch + q * 2048, plo, P[q]);
   }
 }
 
@@ -420,14 +424,14 @@ struct StreamPos {
   int u, left, p;
 };
 
-// One unit's loads for one wave (subtile t = wave of both strips of a tile).
-template <int XQ>
+// One unit's loads for one wave (subtile t = wave of each of the NQ strips of a tile).
+template <int XQ, int NQ>
 struct Slot {
-  u32x2 off[2];        // per strip: esc_off of the escape block and of the next one (every lane)
-  u32x4 hi[2];         // 8-bit view: 16 weights of channel lane%32, k half lane/32
-  u32x2 lo[2];         // their low nibbles
-  uint32_t et[2];      // the 4 window tops around the lane's channel (its byte: lane % 4)
-  uint32_t e[2];       // escape entry number `lane` of the block (if any)
+  u32x2 off[NQ];       // per strip: esc_off of the escape block and of the next one (every lane)
+  u32x4 hi[NQ];        // 8-bit view: 16 weights of channel lane%32, k half lane/32
+  u32x2 lo[NQ];        // their low nibbles
+  uint32_t et[NQ];     // the 4 window tops around the lane's channel (its byte: lane % 4)
+  uint32_t e[NQ];      // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ][2];     // x operands that ride with the unit
 };
 
@@ -442,10 +446,10 @@ struct Slot {
 // for. So D units of weight loads stay in flight during that arithmetic. The
 // ring holds D + 2 slots: O runs one slot ahead of W/E, and one slot is being
 // computed.
-template <int XQ>
+template <int XQ, int NQ, int D>
 struct Ring {
-  static constexpr int NS = kDepth + 2;
-  Slot<XQ> s[NS];
+  static constexpr int NS = D + 2;
+  Slot<XQ, NQ> s[NS];
 };
 
 // The Q pass (QP) reads only the 8-bit view of each record; the low nibbles
@@ -453,36 +457,35 @@ struct Ring {
 constexpr uint32_t kMidNibbles = 0x88888888u;
 
 // The per-unit loads shared by both small-m kernels, as two wave-uniform
-// streams. Everything that changes only at a tile (the strips' record
-// resources, window-top offsets, escape-offset resources) is set up at the
-// tile's first unit; per unit the streams only advance scalar offsets.
-//  * W stream (records, window tops, x). Past the slice its resources are
-//    empty: the loads return zeros and move no data. A missing second strip
-//    (odd strip count) has an empty record resource and reads the first
-//    strip's window tops, so it restores finite values; its channels are
-//    never stored.
+// streams. Everything that changes only at a tile (the tile's record resource,
+// window-top and escape-offset positions) is set up at the tile's first unit;
+// per unit the streams only advance scalar offsets.
+//  * W stream (records, window tops, x). The record resource covers the
+//    tile's strips that exist, so a missing strip (the strip count is not a
+//    multiple of NQ) reads zeros; past the slice the resources are empty and
+//    the loads move no data. A missing strip's channels are never stored.
 //  * O stream (escape-block offsets, read by every lane through a resource
 //    that covers esc_off exactly). A missing strip, or a tile past the last,
-//    reads through an empty resource: offsets 0, 0, no escapes.
+//    reads 1 GiB further on, out of range: offsets 0, 0, no escapes.
 //  * E (escape entries): lane l reads entry o0 + l through a resource that
 //    covers the n_esc entries; lanes past the block's count are not used.
-template <int XQ, bool QP = false>
+constexpr uint32_t kOutOfRange = 1u << 30;
+
+template <int XQ, bool QP, int NQ>
 struct UnitLoads {
   const GemmParams& a;
   int wave, RK, S, u1;
   uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4;
-  rsrc_t r_esc, r_off, r_none;
-  rsrc_t r_et;
+  rsrc_t r_esc, r_off, r_et;
   const void* x_base;
   uint32_t x_bytes, x_tile, x_step;
   // W stream
   StreamPos w;
-  rsrc_t rq[2], rx;
-  uint32_t so, sx, sb[2];
+  rsrc_t rt, rx;
+  uint32_t so, sx, sb;
   // O stream
   StreamPos o;
-  rsrc_t ro[2];
-  uint32_t oo;
+  uint32_t oo, om[NQ];
 
   __device__ __forceinline__ UnitLoads(const GemmParams& a_, int wave_, int lane, int u0, int u1_,
                                        const void* xb, uint32_t xbytes, uint32_t xtile, uint32_t xstep)
@@ -497,7 +500,6 @@ struct UnitLoads {
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
     r_off = make_rsrc(a.w.esc_off, (uint32_t)(a.w.nb + 1) * 4u);
-    r_none = make_rsrc(a.w.esc_off, 0u);
     r_et = make_rsrc(a.w.e_top, (uint32_t)a.w.n);
     const int p = u0 / RK, r = u0 - p * RK;
     w = StreamPos{u0, min(RK - r, u1 - u0), p};
@@ -508,16 +510,13 @@ struct UnitLoads {
 
   // The W stream enters tile w.p at record r.
   __device__ __forceinline__ void w_tile(int r) {
-    const int sq = 2 * w.p;
-    const bool has1 = sq + 1 < S;
-    const uint8_t* base = a.w.rec + (int64_t)sq * strip_bytes;
-    rq[0] = make_rsrc(base, strip_bytes);
-    rq[1] = make_rsrc(base + strip_bytes, has1 ? strip_bytes : 0u);
+    const int sq = NQ * w.p;
+    const int ns = min(NQ, S - sq);
+    rt = make_rsrc(a.w.rec + (int64_t)sq * strip_bytes, (uint32_t)ns * strip_bytes);
     rx = make_rsrc(x_base, x_bytes);
     so = (uint32_t)r * kRecBytes;
     sx = x_tile + (uint32_t)r * x_step;
-    sb[0] = (uint32_t)sq * kStrip;
-    sb[1] = has1 ? sb[0] + kStrip : sb[0];
+    sb = (uint32_t)sq * kStrip;
   }
   __device__ __forceinline__ void w_next() {
     ++w.u;
@@ -525,7 +524,8 @@ struct UnitLoads {
     sx += x_step;
     if (--w.left == 0) {
       if (w.u >= u1) {  // past the slice
-        rq[0] = rq[1] = rx = r_none;
+        rt = make_rsrc(a.w.rec, 0u);
+        rx = rt;
         w.left = 1 << 30;
       } else {
         ++w.p;
@@ -536,10 +536,10 @@ struct UnitLoads {
   }
   // The O stream enters tile o.p at record r: escape block (strip, r, wave).
   __device__ __forceinline__ void o_tile(int r) {
-    const int sq = 2 * o.p;
-    ro[0] = sq < S ? r_off : r_none;
-    ro[1] = sq + 1 < S ? r_off : r_none;
-    oo = (uint32_t)(((sq * RK + r) * 8 + wave) * 4);
+    const int sq = NQ * o.p;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) om[q] = (uint32_t)(q * RK) * 32u + (sq + q < S ? 0u : kOutOfRange);
+    oo = (uint32_t)((((sq < S ? sq : 0) * RK + r) * 8 + wave) * 4);
   }
   __device__ __forceinline__ void o_next() {
     ++o.u;
@@ -551,27 +551,28 @@ struct UnitLoads {
     }
   }
 
-  __device__ __forceinline__ void issue_off(Slot<XQ>& s) const {
-    s.off[0] = bload2(ro[0], 0u, oo);
-    s.off[1] = bload2(ro[1], 0u, oo + (uint32_t)RK * 32u);
-  }
-  __device__ __forceinline__ void issue_w(Slot<XQ>& s) const {
+  __device__ __forceinline__ void issue_off(Slot<XQ, NQ>& s) const {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      s.hi[q] = bload4<kNonTemporal>(rq[q], v_hi, so);
+    for (int q = 0; q < NQ; ++q) s.off[q] = bload2(r_off, 0u, oo + om[q]);
+  }
+  __device__ __forceinline__ void issue_w(Slot<XQ, NQ>& s) const {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint32_t sq = so + (uint32_t)q * strip_bytes;
+      s.hi[q] = bload4<kNonTemporal>(rt, v_hi, sq);
       if constexpr (QP) {
         s.lo[q] = u32x2{kMidNibbles, kMidNibbles};
       } else {
-        s.lo[q] = bload2<kNonTemporal>(rq[q], v_lo, so);
+        s.lo[q] = bload2<kNonTemporal>(rt, v_lo, sq);
       }
       // a whole dword: a byte load's result would be widened where the ring
       // wraps round, which makes the compiler wait for the load right there
-      s.et[q] = bload1(r_et, v_c4, sb[q]);
+      s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * kStrip);
     }
   }
-  __device__ __forceinline__ void issue_e(Slot<XQ>& s) const {
+  __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) s.e[q] = bload1(r_esc, s.off[q].x * 4u + v_l4, 0);
+    for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off[q].x * 4u + v_l4, 0);
   }
 };
 
@@ -579,30 +580,30 @@ struct UnitLoads {
 // step inside the unrolled body would make the compiler's load-wait counts
 // assume fewer loads in flight and wait for the next units' loads as well),
 // and a guarded tail of fewer than NS units.
-template <int XQ, typename LoadsT, typename XF, typename StepF>
+template <int XQ, int NQ, int D, typename LoadsT, typename XF, typename StepF>
 __device__ __forceinline__ void walk_slice(LoadsT& L, int u0, int u1, XF&& issue_x, StepF&& step) {
-  Ring<XQ> ring;
-  constexpr int NS = Ring<XQ>::NS;
-  static_for<kDepth + 1>([&](auto jc) {
+  Ring<XQ, NQ, D> ring;
+  constexpr int NS = Ring<XQ, NQ, D>::NS;
+  static_for<D + 1>([&](auto jc) {
     L.issue_off(ring.s[decltype(jc)::value]);
     L.o_next();
   });
-  static_for<kDepth>([&](auto jc) {
+  static_for<D>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     L.issue_w(ring.s[j]);
     issue_x(ring.s[j]);
     L.w_next();
   });
-  static_for<kDepth>([&](auto jc) { L.issue_e(ring.s[decltype(jc)::value]); });
+  static_for<D>([&](auto jc) { L.issue_e(ring.s[decltype(jc)::value]); });
   auto iteration = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    L.issue_off(ring.s[(k + kDepth + 1) % NS]);
+    L.issue_off(ring.s[(k + D + 1) % NS]);
     L.o_next();
-    L.issue_w(ring.s[(k + kDepth) % NS]);
-    issue_x(ring.s[(k + kDepth) % NS]);
+    L.issue_w(ring.s[(k + D) % NS]);
+    issue_x(ring.s[(k + D) % NS]);
     L.w_next();
     step(ring.s[k]);
-    L.issue_e(ring.s[(k + kDepth) % NS]);
+    L.issue_e(ring.s[(k + D) % NS]);
   };
   int base = u0;
   for (; base + NS <= u1; base += NS) static_for<NS>(iteration);
@@ -625,12 +626,19 @@ __device__ __forceinline__ uint32_t bias2_of_top(uint32_t et4, int lane) {
 
 // ============================================================================ MFMA path (m >= 16)
 
-template <int MT, int EPI, bool QP>
+template <int MT, int EPI, bool QP, int NQ>
 __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   // x fragments of the MT tiles of 32 rows ride in the load ring.
   static_assert(MT >= 1 && MT <= 2, "small-m kernel: at most 64 rows");
   constexpr int XQ = MT;
-  __shared__ __align__(16) float lds[kMfmaLdsFloats];
+  // NQ strips per tile (each x load serves NQ strips). With 4 strips the ring
+  // is one unit deep to stay within the register file; measured at 32 rows
+  // that was slower than 2 strips two units deep, which is the one selected.
+  constexpr int D = NQ == 4 ? 1 : 2;
+  constexpr int TC = NQ * kStrip;       // channels per tile
+  constexpr int RS = TC + 4;            // reduction slot row stride (floats)
+  constexpr int SF = 32 * RS;           // reduction slot (one wave, one M-tile)
+  __shared__ __align__(16) float lds[kNW * SF];  // reduction slots; patch buffers alias them
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -638,14 +646,15 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   const int g = logical_wg(blockIdx.x, a.G);
   const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
-  char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
+  char* patch = reinterpret_cast<char*>(lds) + wave * (NQ * 2048);
+  static_assert(kNW * NQ * 2048 <= kNW * SF * 4, "patch buffers fit in the reduction slots");
 
-  f32x16 acc[2][MT];
+  f32x16 acc[NQ][MT];
   unsigned long long run[MT];  // argmax: best key of row mt * 32 + tid / 16 over the slice's whole tiles
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) run[mt] = 0;
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -653,12 +662,12 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
   // x fragment (record r, subtile t, tile mt, half h) of the fragment buffer
   // is at ((r * 8 + t) * MT + mt) * 2048 + h * 1024.
-  UnitLoads<XQ, QP> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
+  UnitLoads<XQ, QP, NQ> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
                       (uint32_t)(wave * MT * 2048), (uint32_t)(MT * 8 * 2048));
   const uint32_t plo = patch_lane_off(lane);
   const uint32_t v_x = (uint32_t)lane * 16u;
 
-  auto issue_x = [&](Slot<XQ>& s) __attribute__((always_inline)) {
+  auto issue_x = [&](Slot<XQ, NQ>& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < XQ; ++mt) {
       s.xv[mt][0] = bload4(L.rx, v_x + (uint32_t)(mt * 2048), L.sx);
@@ -676,38 +685,43 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       constexpr int mt = decltype(mtc)::value;
       lds_barrier();  // the slots (and patch buffers) are free
       {
-        float* dst = lds + wave * kSlotFloats;
+        float* dst = lds + wave * SF;
         const int ml = lane & 31, hf = lane >> 5;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<float4*>(dst + ml * kRedStride + 32 * q + 8 * rb + 4 * hf) =
+            *reinterpret_cast<float4*>(dst + ml * RS + 32 * q + 8 * rb + 4 * hf) =
                 make_float4(acc[q][mt][4 * rb], acc[q][mt][4 * rb + 1], acc[q][mt][4 * rb + 2],
                             acc[q][mt][4 * rb + 3]);
       }
       lds_barrier();
-      const int ml = tid >> 4, c4 = (tid & 15) * 4;  // 32 rows x 16 channel quads = kNT
-      const float* b = lds + ml * kRedStride + c4;
-      float4 sw[kNW];
+      // 32 rows x 16 channel quads per pass: 16 consecutive threads hold 64
+      // channels of one row
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) sw[w] = *reinterpret_cast<const float4*>(b + w * kSlotFloats);
-      const float4 v = f4add(f4add(f4add(sw[0], sw[4]), f4add(sw[1], sw[5])),
-                             f4add(f4add(sw[2], sw[6]), f4add(sw[3], sw[7])));
-      const int m = mt * 32 + ml;
-      if (whole) {
-        if constexpr (EPI == kEpiArgmax) {
-          run[mt] = kmax(run[mt], row_key4(a, m, p * 64 + c4, v));
-        } else {
-          emit4<EPI>(a, tid, m, p * 64 + c4, v);
+      for (int h = 0; h < NQ / 2; ++h) {
+        const int ml = tid >> 4, c4 = h * 64 + (tid & 15) * 4;
+        const float* b = lds + ml * RS + c4;
+        float4 sw[kNW];
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) sw[w] = *reinterpret_cast<const float4*>(b + w * SF);
+        const float4 v = f4add(f4add(f4add(sw[0], sw[4]), f4add(sw[1], sw[5])),
+                               f4add(f4add(sw[2], sw[6]), f4add(sw[3], sw[7])));
+        const int m = mt * 32 + ml;
+        if (whole) {
+          if constexpr (EPI == kEpiArgmax) {
+            run[mt] = kmax(run[mt], row_key4(a, m, p * TC + c4, v));
+          } else {
+            emit4<EPI>(a, tid, m, p * TC + c4, v);
+          }
+        } else if (m < a.M) {
+          store_partial<TC>(a, slot, m, c4, v);
         }
-      } else if (m < a.M) {
-        store_partial<64>(a, slot, m, c4, v);
       }
     });
     lds_barrier();
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -716,7 +730,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
   // ---- arithmetic of one unit
   TileCursor cur{u0 / RK, min(RK - (u0 - (u0 / RK) * RK), u1 - u0), u0};
-  auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
+  auto step = [&](const Slot<XQ, NQ>& s) __attribute__((always_inline)) {
     if (cur.left == 0) {
       flush(cur.p);
       ++cur.p;
@@ -724,26 +738,26 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     }
     --cur.left;
     ++cur.u;
-    uint32_t P[2][8];
-    restore_unit(s, bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane), patch, plo, lane, L.r_esc, P);
-    const u32x4 (&xl)[MT][2] = s.xv;
-    const bf16x8 a00 = __builtin_bit_cast(bf16x8, u32x4{P[0][0], P[0][1], P[0][2], P[0][3]});
-    const bf16x8 a01 = __builtin_bit_cast(bf16x8, u32x4{P[0][4], P[0][5], P[0][6], P[0][7]});
-    const bf16x8 a10 = __builtin_bit_cast(bf16x8, u32x4{P[1][0], P[1][1], P[1][2], P[1][3]});
-    const bf16x8 a11 = __builtin_bit_cast(bf16x8, u32x4{P[1][4], P[1][5], P[1][6], P[1][7]});
+    uint32_t bias[NQ];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, xl[mt][0]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, xl[mt][1]);
-      acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a00, b0, acc[0][mt], 0, 0, 0);
-      acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a01, b1, acc[0][mt], 0, 0, 0);
-      acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, b0, acc[1][mt], 0, 0, 0);
-      acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, b1, acc[1][mt], 0, 0, 0);
+    for (int q = 0; q < NQ; ++q) bias[q] = bias2_of_top(s.et[q], lane);
+    uint32_t P[NQ][8];
+    restore_unit<NQ>(s, bias, patch, plo, lane, L.r_esc, P);
+    const u32x4 (&xl)[MT][2] = s.xv;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{P[q][0], P[q][1], P[q][2], P[q][3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{P[q][4], P[q][5], P[q][6], P[q][7]});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8, xl[mt][0]), acc[q][mt], 0, 0, 0);
+        acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8, xl[mt][1]), acc[q][mt], 0, 0, 0);
+      }
     }
   };
 
   if (u0 < u1) {
-    walk_slice<XQ>(L, u0, u1, issue_x, step);
+    walk_slice<XQ, NQ, D>(L, u0, u1, issue_x, step);
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax) {
@@ -751,7 +765,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     for (int mt = 0; mt < MT; ++mt)
       if ((tid & 15) == 0 && run[mt]) atomicMax(&a.keys[mt * 32 + (tid >> 4)], run[mt]);
   }
-  finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
+  finish_slice<EPI, kNT, TC, 2>(a, tid, u0, u1, &s_last);
 }
 
 // ============================================================================ VALU path (m < 16)
@@ -784,7 +798,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     for (int m = 0; m < MV; ++m) acc[q][m] = 0.f;
 
   // x rows >= M read 0 (voffset past the range); a record's x starts 512 bytes on.
-  UnitLoads<XQ, QP> L(a, wave, lane, u0, u1, a.x, (uint32_t)a.M * (uint32_t)a.K * 2u, 0u, 512u);
+  UnitLoads<XQ, QP, 2> L(a, wave, lane, u0, u1, a.x, (uint32_t)a.M * (uint32_t)a.K * 2u, 0u, 512u);
   const uint32_t plo = patch_lane_off(lane);
   // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
   const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
@@ -794,7 +808,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // subtile's 64 (rows >= m read 0)
   const uint32_t v_xp = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)(wave * kSubK) * 2u + (uint32_t)(lane & 3) * 16u;
   char* xw = xlds + (kXLds ? wave * 1024 : 0);
-  auto issue_x = [&](Slot<XQ>& s) __attribute__((always_inline)) {
+  auto issue_x = [&](Slot<XQ, 2>& s) __attribute__((always_inline)) {
     if constexpr (kXLds) {
       s.xv[0][0] = bload4(L.rx, v_xp, L.sx);
     } else {
@@ -853,7 +867,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   };
 
   TileCursor cur{u0 / RK, min(RK - (u0 - (u0 / RK) * RK), u1 - u0), u0};
-  auto step = [&](const Slot<XQ>& s) __attribute__((always_inline)) {
+  auto step = [&](const Slot<XQ, 2>& s) __attribute__((always_inline)) {
     if (cur.left == 0) {
       flush(cur.p);
       ++cur.p;
@@ -861,8 +875,9 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     }
     --cur.left;
     ++cur.u;
+    const uint32_t bias[2] = {bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane)};
     uint32_t P[2][8];
-    restore_unit(s, bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane), patch, plo, lane, L.r_esc, P);
+    restore_unit<2>(s, bias, patch, plo, lane, L.r_esc, P);
     if constexpr (kXLds) {
       wave_lds_order();  // the previous unit's reads of the buffer come first
       *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
@@ -885,7 +900,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   };
 
   if (u0 < u1) {
-    walk_slice<XQ>(L, u0, u1, issue_x, step);
+    walk_slice<XQ, 2, kDepth>(L, u0, u1, issue_x, step);
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax) {
@@ -1281,8 +1296,8 @@ KernelSel select_kernel(int M) {
     }
   }
   if (M >= 16) {
-    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP>), 1, kNT};
-    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP>), 2, kNT};
+    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 2>), 1, kNT};
+    return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP, 2>), 2, kNT};
   }
   const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   switch (mv) {
@@ -1304,7 +1319,7 @@ constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + argmax keys 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
   const bool big = m > kSmallMaxRows;
-  const int64_t tc = big ? kBigTC : 2 * kStrip;
+  const int64_t tc = big ? kBigTC : 2 * kStrip;  // channels per tile of the kernel select_kernel picks
   const int64_t S = n / kStrip, sp = tc / kStrip, P = (S + sp - 1) / sp, RK = k / kRecK;
   const int64_t mt = (!big && m >= 16) ? (m + 31) / 32 : 0;
   const int64_t U = P * RK;
