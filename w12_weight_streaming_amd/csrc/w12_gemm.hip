@@ -597,11 +597,15 @@ __device__ __forceinline__ void walk_slice(LoadsT& L, int u0, int u1, XF&& issue
   static_for<D>([&](auto jc) { L.issue_e(ring.s[decltype(jc)::value]); });
   auto iteration = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
+    // a wave whose unit has arrived issues the next loads ahead of the other
+    // waves' arithmetic, keeping the memory pipeline full
+    __builtin_amdgcn_s_setprio(2);
     L.issue_off(ring.s[(k + D + 1) % NS]);
     L.o_next();
     L.issue_w(ring.s[(k + D) % NS]);
     issue_x(ring.s[(k + D) % NS]);
     L.w_next();
+    __builtin_amdgcn_s_setprio(0);
     step(ring.s[k]);
     L.issue_e(ring.s[(k + D) % NS]);
   };
