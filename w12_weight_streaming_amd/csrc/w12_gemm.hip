@@ -170,7 +170,11 @@ __device__ __forceinline__ unsigned long long row_key4(const GemmParams& a, int 
   return row16_max(best);
 }
 __device__ __forceinline__ unsigned long long kmax(unsigned long long x, unsigned long long y) { return x > y ? x : y; }
-
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
 // Final value of 4 consecutive channels (n .. n+3) of row m. For the argmax
 // epilogue, 16 consecutive threads of a wave hold one row's 64 channels.
 //
@@ -297,7 +301,16 @@ __device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, in
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const int e = e0 + j * NT + tid;
-        emit4<EPI>(a, tid, e / Q, p * TC + (e % Q) * 4, v[j]);
+        if constexpr (EPI == kEpiArgmax) {
+          // Q consecutive threads hold one row: maximise over all of them
+          // (Q <= 64, one wave) before the one atomic of the row
+          unsigned long long key = row_key4(a, e / Q, p * TC + (e % Q) * 4, v[j]);
+          if constexpr (Q >= 32) key = kmax(key, shfl_xor64(key, 16));
+          if constexpr (Q >= 64) key = kmax(key, shfl_xor64(key, 32));
+          if ((e % Q) == 0 && key) atomicMax(&a.keys[e / Q], key);
+        } else {
+          emit4<EPI>(a, tid, e / Q, p * TC + (e % Q) * 4, v[j]);
+        }
       }
     }
     if (tid == 0) atomicExch(&a.tile_cnt[p], 0u);
@@ -1253,9 +1266,22 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
 
   if (u0 < u1) walk_big8<MT>(L, lane, u0, u1, RK, xload, xstore, flush, step);
   if constexpr (EPI == kEpiArgmax) {
+    // the 4 strip waves' keys of each row are maximised through LDS first:
+    // one device-scope atomic per row and workgroup
+    static_assert(Lds::kBytes >= MT * 4 * 32 * 8, "key buffer fits");
+    unsigned long long* kb = reinterpret_cast<unsigned long long*>(lds);
+    __syncthreads();
+    if (kg == 0 && lane < 32) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      if (run[mt]) atomicMax(&a.keys[mt * 32 + (lane & 31)], run[mt]);
+      for (int mt = 0; mt < MT; ++mt) kb[(mt * 4 + sw) * 32 + lane] = run[mt];
+    }
+    __syncthreads();
+    for (int r = tid; r < MT * 32; r += kB8NT) {
+      unsigned long long b = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b = kmax(b, kb[((r >> 5) * 4 + q) * 32 + (r & 31)]);
+      if (b) atomicMax(&a.keys[r], b);
+    }
   }
   finish_slice<EPI, kB8NT, kBigTC, 4>(a, tid, u0, u1, &s_last);
 }
