@@ -11,8 +11,10 @@ Sources (the pages these functions follow):
        section 1.1 (greedy acceptance, tau range), 1.2 (lossless / exact pass,
        near-ties from floating-point order), 2.4 (discarded-candidate example),
        4.1 (W12 format, record, stream-K determinism, LM head argmax),
-       4.3 (tree verification accepts the longest matching path + bonus;
-       8-bit view read by the Q pass).
+       4.2 (best-first tree: parent-conditioned edge scores, the N nodes
+       with the highest path score), 4.3 (tree verification accepts the
+       longest matching path + bonus; 8-bit view read by the Q pass),
+       4.4 (shared node budget across the requests of a step).
   [S2] the same paper's digest page (agihunt.info), W12 paragraph: sign +
        4-bit exponent offset + all 7 mantissa bits; load-time check.
   [S3] "Speculative decoding" (poot-llm docs), section "What a round

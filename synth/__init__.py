@@ -109,3 +109,33 @@ def random_tree(num_nodes: int, max_depth: int, row_argmax: np.ndarray,
             t = int(rng.integers(0, vocab - 1))
             token[i] = t + 1 if t >= target else t
     return parent, token
+
+
+def draft_lattice(num_req: int, positions: int, k: int, seed: int, *, vocab: int = 152064,
+                  temperature: float = 2.0, depths=None, quantum: float | None = None):
+    """Candidate lattices of a step, one per request (the drafter's output).
+
+    Per request r, position d, parent candidate i: edge logits
+    z ~ N(0, temperature^2) over the K child candidates, turned into a
+    log-softmax in float64 and stored as float32 (lp [R, D, K, K]). With
+    ``quantum`` the logits are rounded to multiples of it first, which makes
+    equal edge scores (and equal path scores) common. Candidate tokens are K
+    distinct vocabulary ids per position (tok [R, D, K]); root tokens are
+    uniform ids (roots [R]). ``depths`` (positions drafted per request)
+    defaults to a uniform choice among 16, 12 and 8, capped at ``positions``.
+    Returns (lp, tok, depths, roots).
+    """
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0.0, temperature, (num_req, positions, k, k))
+    if quantum:
+        z = np.round(z / quantum) * quantum
+    z = z - z.max(axis=-1, keepdims=True)
+    lp = (z - np.log(np.exp(z).sum(axis=-1, keepdims=True))).astype(np.float32)
+    lp = np.minimum(lp, np.float32(0.0))
+    tok = np.stack([np.stack([rng.choice(vocab, k, replace=False) for _ in range(positions)])
+                    for _ in range(num_req)]).astype(np.int32)
+    if depths is None:
+        depths = np.minimum(rng.choice([16, 12, 8], num_req), positions)
+    depths = np.asarray(depths, dtype=np.int32)
+    roots = rng.integers(0, vocab, num_req).astype(np.int32)
+    return lp, tok, depths, roots
