@@ -179,6 +179,42 @@ w12_status w12_head_argmax_qpass(const w12_matrix *head, const uint16_t *x, int6
                                  hipStream_t stream);
 
 /*
+ * w12_tree_build -- best-first draft trees under one shared row budget
+ * ([S1] 4.2: every edge scored by the log-softmax of the child given its
+ * parent, the nodes of highest path score kept; [S1] 4.4: one node budget
+ * shared by all requests of a step, filled from the highest path score down,
+ * each request's share a prefix-closed tree).
+ *   num_req R in [1, 128]; positions D in [1, 16]; k K in [1, 16].
+ *   lp    [R][D][K][K] fp32: lp[r][d][i][j] = edge score from candidate i of
+ *         position d - 1 (the root for d = 0, row i = 0) to candidate j of
+ *         position d; expected <= 0 (a log-softmax over j), finite.
+ *   tok   [R][D][K] int32 candidate tokens; depth [R] int32 positions drafted
+ *         per request (values outside [0, D] are clamped); root [R] int32
+ *         committed token of each request.
+ *   budget rows in all, roots included: R <= budget, budget - R <= 1023 and
+ *         R * (budget - R) <= 8192.
+ * Order: path score (the binary32 sum of edge scores, accumulated from the
+ * root in path order) highest first, then depth, then request index, then the
+ * path of child ranks (a parent's children ranked by edge score, equal scores
+ * by candidate index).
+ * Output (device memory, caller-owned, the layout tree_accept reads):
+ *   node_off [R+1]; then per request its root row (parent -1, token root[r],
+ *   depth 0, score 0) followed by its draft nodes in that order, parent local
+ *   to the request; parent, token, node_depth, score hold node_off[R] rows
+ *   (at most budget; fewer when the lattices run out of nodes). node_depth and
+ *   score may be NULL.
+ * Workspace: w12_tree_build_workspace bytes, 16-byte aligned, content ignored.
+ * Errors: W12_EINVAL for shapes or pointers outside the above, W12_ENOSPC for
+ * a small workspace, W12_EHIP for a launch error.
+ */
+w12_status w12_tree_build_workspace(int32_t num_req, int32_t budget, size_t *bytes);
+w12_status w12_tree_build(int32_t num_req, int32_t positions, int32_t k, const float *lp,
+                          const int32_t *tok, const int32_t *depth, const int32_t *root,
+                          int32_t budget, void *ws, size_t ws_bytes, int32_t *node_off,
+                          int32_t *parent, int32_t *token, int32_t *node_depth, float *score,
+                          hipStream_t stream);
+
+/*
  * tree_accept -- greedy tree verification ([S1] 1.1, 4.3; [S3]).
  * Trees are concatenated: tree t owns nodes [node_off[t], node_off[t+1]),
  * node_off[0] = 0, node_off[num_trees] = total_nodes; node i of a tree is

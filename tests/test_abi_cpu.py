@@ -80,6 +80,26 @@ def test_invalid_arguments_rejected_before_launch(L):
     assert L.tree_accept(0, null, 0, null, null, null, null, null, null, null) == w.W12_OK
 
 
+def test_tree_build_limits_rejected_before_launch(L):
+    import w12_weight_streaming_amd as w
+    EINVAL, ENOSPC = w.W12_EINVAL, w.W12_ENOSPC
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    sz = ctypes.c_size_t(0)
+    assert L.w12_tree_build_workspace(24, 192, ctypes.byref(sz)) == w.W12_OK and sz.value >= 24 * 168 * 16
+    for R, budget in ((0, 8), (129, 200), (4, 3), (1, 1 + 1024), (16, 16 + 600)):
+        assert L.w12_tree_build_workspace(R, budget, ctypes.byref(sz)) == EINVAL, (R, budget)
+
+    def call(R=24, D=16, K=16, budget=192, ws=fake, wsb=1 << 20, lp=fake):
+        return L.w12_tree_build(R, D, K, lp, fake, fake, fake, budget, ws, wsb, fake, fake, fake, null, null, null)
+    assert call(D=0) == EINVAL and call(D=17) == EINVAL
+    assert call(K=0) == EINVAL and call(K=17) == EINVAL
+    assert call(budget=23) == EINVAL
+    assert call(lp=null) == EINVAL
+    assert call(ws=ctypes.c_void_p(0x1008)) == EINVAL  # workspace not 16-byte aligned
+    assert call(wsb=100) == ENOSPC
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import w12_weight_streaming_amd as w

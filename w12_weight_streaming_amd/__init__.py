@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
             "w12_gemm_qpass": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
             "w12_head_argmax_qpass": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "tree_accept": (ctypes.c_int, [i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+            "w12_tree_build_workspace": (ctypes.c_int, [i32, i32, ctypes.POINTER(sz)]),
+            "w12_tree_build": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp, vp,
+                                              vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -78,7 +81,7 @@ def exported_symbols():
     return ["w12_strerror", "w12_abi_version", "w12_num_blocks", "w12_pack_plan", "w12_pack",
             "w12_decode", "w12_check", "w12_gemm_workspace", "w12_gemm",
             "w12_head_argmax_workspace", "w12_head_argmax", "w12_gemm_qpass",
-            "w12_head_argmax_qpass", "tree_accept"]
+            "w12_head_argmax_qpass", "tree_accept", "w12_tree_build_workspace", "w12_tree_build"]
 
 
 def _ok(status: int, what: str):
@@ -265,3 +268,34 @@ def tree_accept(node_off: torch.Tensor, parent: torch.Tensor, token: torch.Tenso
     _ok(lib().tree_accept(T, _ptr(node_off), total, _ptr(parent), _ptr(token), _ptr(argmax),
                           _ptr(acc), _ptr(path), _ptr(bonus), _stream(dev)), "tree_accept")
     return acc, path, bonus
+
+
+def w12_tree_build(lp: torch.Tensor, tok: torch.Tensor, depth: torch.Tensor, root: torch.Tensor,
+                   budget: int, ws: torch.Tensor | None = None):
+    """Best-first draft trees of R requests under one shared row budget.
+
+    lp [R, D, K, K] fp32 edge scores, tok [R, D, K] int32, depth [R] int32,
+    root [R] int32 (device tensors). Returns (node_off [R+1], parent, token,
+    node_depth, score), the row arrays trimmed to node_off[R] rows."""
+    _need(lp, torch.float32, "lp", 4)
+    _need(tok, torch.int32, "tok", 3)
+    _need(depth, torch.int32, "depth", 1)
+    _need(root, torch.int32, "root", 1)
+    R, D, K, K2 = lp.shape
+    if K2 != K or tuple(tok.shape) != (R, D, K) or depth.numel() != R or root.numel() != R:
+        raise ValueError("w12_tree_build: inconsistent shapes")
+    dev = lp.device
+    need = ctypes.c_size_t(0)
+    _ok(lib().w12_tree_build_workspace(R, budget, ctypes.byref(need)), "w12_tree_build_workspace")
+    if ws is None:
+        ws = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=dev)
+    node_off = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    parent = torch.empty(budget, dtype=torch.int32, device=dev)
+    token = torch.empty(budget, dtype=torch.int32, device=dev)
+    ndepth = torch.empty(budget, dtype=torch.int32, device=dev)
+    score = torch.empty(budget, dtype=torch.float32, device=dev)
+    _ok(lib().w12_tree_build(R, D, K, _ptr(lp), _ptr(tok), _ptr(depth), _ptr(root), budget, _ptr(ws),
+                             ws.numel(), _ptr(node_off), _ptr(parent), _ptr(token), _ptr(ndepth),
+                             _ptr(score), _stream(dev)), "w12_tree_build")
+    n = int(node_off[-1].item())
+    return node_off, parent[:n], token[:n], ndepth[:n], score[:n]

@@ -215,4 +215,33 @@ w12_status tree_accept(int32_t num_trees, const int32_t* node_off, int32_t total
                                     accept_len, path, bonus, stream));
 }
 
+namespace {
+// Limits of the tree builder's kernels: K, D <= 16 (4-bit ranks, 16-level
+// rank paths); R <= 128 and budget - R <= 1023 (request and position fields
+// of the 64-bit selection key); R (budget - R) <= 8192 (keys held in LDS).
+bool tree_build_ok(int32_t R, int32_t D, int32_t K, int32_t budget) {
+  if (R < 1 || R > 128 || D < 1 || D > 16 || K < 1 || K > 16) return false;
+  if (budget < R || budget - R > 1023) return false;
+  return (int64_t)R * (budget - R) <= 8192;
+}
+}  // namespace
+
+w12_status w12_tree_build_workspace(int32_t num_req, int32_t budget, size_t* bytes) {
+  if (!bytes || !tree_build_ok(num_req, 1, 1, budget)) return W12_EINVAL;
+  *bytes = w12::tree_build_ws_bytes(num_req, budget);
+  return W12_OK;
+}
+
+w12_status w12_tree_build(int32_t num_req, int32_t positions, int32_t k, const float* lp, const int32_t* tok,
+                          const int32_t* depth, const int32_t* root, int32_t budget, void* ws,
+                          size_t ws_bytes, int32_t* node_off, int32_t* parent, int32_t* token,
+                          int32_t* node_depth, float* score, hipStream_t stream) {
+  if (!tree_build_ok(num_req, positions, k, budget)) return W12_EINVAL;
+  if (!lp || !tok || !depth || !root || !node_off || !parent || !token || !ws) return W12_EINVAL;
+  if (!aligned(ws, 16) || !aligned(lp, 4)) return W12_EINVAL;
+  if (ws_bytes < w12::tree_build_ws_bytes(num_req, budget)) return W12_ENOSPC;
+  return st(w12::launch_tree_build(num_req, positions, k, lp, tok, depth, root, budget, ws, node_off, parent,
+                                   token, node_depth, score, stream));
+}
+
 }  // extern "C"

@@ -66,6 +66,12 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e
 hipError_t launch_decode(const MatrixArgs& a, uint16_t* out, hipStream_t s);
 hipError_t launch_check(const MatrixArgs& a, const uint16_t* ref, unsigned long long* mism,
                         hipStream_t s);
+// Best-first draft trees under a shared row budget (tree_build.hip).
+size_t tree_build_ws_bytes(int32_t num_req, int32_t budget);
+hipError_t launch_tree_build(int32_t R, int32_t D, int32_t K, const float* lp, const int32_t* tok,
+                             const int32_t* depth, const int32_t* roots, int32_t budget, void* ws,
+                             int32_t* node_off, int32_t* parent, int32_t* token, int32_t* node_depth,
+                             float* score, hipStream_t s);
 hipError_t launch_tree_accept(int32_t num_trees, const int32_t* node_off, int32_t total,
                               const int32_t* parent, const int32_t* token, const int32_t* argmax,
                               int32_t* accept_len, int32_t* path, int32_t* bonus, hipStream_t s);
