@@ -98,12 +98,13 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
-    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep", "qpass"), default="block",
+    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep", "qpass", "tree"), default="block",
                     help="block: one 27B-class block + LM head at M=32 (the headline line); "
                          "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
                          "and 2%% outliers; stack: 64 blocks in sequence at M=32; "
                          "sweep: Wgate|Wup 34816x5120 over M = 1 ... 192; "
-                         "qpass: the block step through the Q pass (8-bit view only)")
+                         "qpass: the block step through the Q pass (8-bit view only); "
+                         "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,6 +133,8 @@ def main():
         return run_sweep(args, w12, synth, torch, dev)
     if args.workload == "qpass":
         return run_qpass(args, w12, synth, torch, dev)
+    if args.workload == "tree":
+        return run_tree(args, w12, synth, torch, dev)
 
     mats, pack_gbps = build_block(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
@@ -351,6 +354,48 @@ def run_batched(args, w12, synth, torch, dev):
                              "frac": round(gbps / HBM_PEAK_GBPS, 4)},
                      "mfma_bf16": {"achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_tree(args, w12, synth, torch, dev):
+    """Best-first draft trees on 16-position x top-16 lattices: 24 requests
+    (drafting 16, 12 or 8 positions) sharing 192 rows, and one request with a
+    32-row tree; device time per build, with the oracle's time beside it."""
+    import time
+    cases = {"shared_24x192": (24, 192, 1_000_000 * 6), "single_32": (1, 32, 1_000_000 * 6 + 1)}
+    res = {}
+    for name, (R, budget, seed) in cases.items():
+        lp, tok, depths, roots = synth.draft_lattice(R, 16, 16, seed, depths=None if R > 1 else [16])
+        import ctypes
+        lp_d, tok_d, dep_d, root_d = [torch.from_numpy(a).to(dev) for a in (lp, tok, depths, roots)]
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        outs = [torch.empty(n, dtype=torch.int32, device=dev) for n in (R + 1, budget, budget, budget)]
+        score = torch.empty(budget, dtype=torch.float32, device=dev)
+        L = w12.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+        def build(i):
+            st = L.w12_tree_build(R, 16, 16, P(lp_d), P(tok_d), P(dep_d), P(root_d), budget, P(ws), ws.numel(),
+                                  P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), P(score), stream)
+            assert st == 0, st
+        for _ in range(args.warmup):
+            build(0)
+        torch.cuda.synchronize()
+        us = min(time_events(build, args.steps) for _ in range(3))
+        t0 = time.perf_counter()
+        from oracle import tree_build as TB
+        TB.shared_budget(lp, tok, depths, roots, budget)
+        res[name] = {"requests": R, "rows": budget, "us": round(us, 2),
+                     "oracle_cpu_us": round((time.perf_counter() - t0) * 1e6, 1)}
+    line = {
+        "metric": "best-first draft tree build time (16 positions x top-16 lattice)", "value": res["shared_24x192"]["us"],
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["shared_24x192"]["us"] / 1000.0, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "24 requests sharing 192 rows (value) and one 32-row tree, 16 x 16 lattices"},
+        "cases": res,
     }
     print(json.dumps(line), flush=True)
 

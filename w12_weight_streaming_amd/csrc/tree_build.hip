@@ -80,14 +80,17 @@ __global__ __launch_bounds__(64) void tree_search_kernel(const float* __restrict
   // ahead of each one (higher score, or equal score and lower index)
   for (int row = lane; row < D * K; row += 64) {
     const float* v = L + (size_t)row * K;
-    for (int j = 0; j < K; ++j) {
-      const float x = v[j];
+    float x[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) x[j] = j < K ? v[j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= K) break;
       int rank = 0;
-      for (int q = 0; q < K; ++q) {
-        const float y = v[q];
-        rank += (y > x || (y == x && q < j)) ? 1 : 0;
-      }
-      s_lp[row * kMaxK + rank] = x;
+#pragma unroll
+      for (int q = 0; q < kMaxK; ++q)
+        rank += (q < K && (x[q] > x[j] || (x[q] == x[j] && q < j))) ? 1 : 0;
+      s_lp[row * kMaxK + rank] = x[j];
       s_slot[row * kMaxK + rank] = (uint8_t)j;
     }
   }
