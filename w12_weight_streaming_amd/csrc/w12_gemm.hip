@@ -170,6 +170,18 @@ __device__ __forceinline__ unsigned long long row_key4(const GemmParams& a, int 
   return row16_max(best);
 }
 __device__ __forceinline__ unsigned long long kmax(unsigned long long x, unsigned long long y) { return x > y ? x : y; }
+// Argmax keys: one copy per XCD (workgroup b runs on XCD b % 8) and one
+// 128-byte line per row, so the grid's per-row atomics spread over 8 x M
+// lines instead of queueing on the two lines 32 packed keys would share. The
+// last workgroup takes the maximum of the 8 copies (max is order-free, so the
+// result does not depend on which XCD ran what).
+constexpr int kKeyCopies = 8;
+constexpr int kKeyRows = 256;    // >= rows per launch
+constexpr int kKeyStride = 16;   // u64 per row: one 128-byte line
+static_assert(kKeyRows >= kRowsPerLaunch, "a key row for every row of a launch");
+__device__ __forceinline__ unsigned long long* key_slot(const GemmParams& a, int m) {
+  return a.keys + ((int)(blockIdx.x % kKeyCopies) * kKeyRows + m) * kKeyStride;
+}
 __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
   const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
@@ -198,7 +210,7 @@ __device__ __forceinline__ void emit4(const GemmParams& a, int tid, int m, int n
     }
   } else {
     const unsigned long long best = row_key4(a, m, n, v);
-    if ((tid & 15) == 0 && best) atomicMax(&a.keys[m], best);
+    if ((tid & 15) == 0 && best) atomicMax(key_slot(a, m), best);
   }
 }
 
@@ -307,7 +319,7 @@ __device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, in
           unsigned long long key = row_key4(a, e / Q, p * TC + (e % Q) * 4, v[j]);
           if constexpr (Q >= 32) key = kmax(key, shfl_xor64(key, 16));
           if constexpr (Q >= 64) key = kmax(key, shfl_xor64(key, 32));
-          if ((e % Q) == 0 && key) atomicMax(&a.keys[e / Q], key);
+          if ((e % Q) == 0 && key) atomicMax(key_slot(a, e / Q), key);
         } else {
           emit4<EPI>(a, tid, e / Q, p * TC + (e % Q) * 4, v[j]);
         }
@@ -329,7 +341,12 @@ __device__ __forceinline__ void finish_grid(const GemmParams& a, int tid, int* s
     __syncthreads();
     if (*s_last) {
       for (int m = tid; m < a.M; m += NT) {
-        const unsigned long long k = atomicExch(&a.keys[m], 0ull);
+        unsigned long long c[kKeyCopies];
+#pragma unroll
+        for (int x = 0; x < kKeyCopies; ++x) c[x] = atomicExch(a.keys + (x * kKeyRows + m) * kKeyStride, 0ull);
+        unsigned long long k = c[0];
+#pragma unroll
+        for (int x = 1; x < kKeyCopies; ++x) k = kmax(k, c[x]);
         a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
         if (a.maxval) a.maxval[m] = key_float((uint32_t)(k >> 32));
       }
@@ -780,7 +797,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   if constexpr (EPI == kEpiArgmax) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      if ((tid & 15) == 0 && run[mt]) atomicMax(&a.keys[mt * 32 + (tid >> 4)], run[mt]);
+      if ((tid & 15) == 0 && run[mt]) atomicMax(key_slot(a, mt * 32 + (tid >> 4)), run[mt]);
   }
   finish_slice<EPI, kNT, TC, 2>(a, tid, u0, u1, &s_last);
 }
@@ -921,7 +938,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax) {
-    if ((tid & 15) == 0 && tid < MV * 16 && run) atomicMax(&a.keys[tid >> 4], run);
+    if ((tid & 15) == 0 && tid < MV * 16 && run) atomicMax(key_slot(a, tid >> 4), run);
   }
   finish_slice<EPI, kNT, 64, 2>(a, tid, u0, u1, &s_last);
 }
@@ -1280,7 +1297,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
       unsigned long long b = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) b = kmax(b, kb[((r >> 5) * 4 + q) * 32 + (r & 31)]);
-      if (b) atomicMax(&a.keys[r], b);
+      if (b) atomicMax(key_slot(a, r), b);
     }
   }
   finish_slice<EPI, kB8NT, kBigTC, 4>(a, tid, u0, u1, &s_last);
@@ -1344,7 +1361,8 @@ KernelSel select_kernel(int M) {
 }  // namespace
 
 constexpr size_t kCounterBytes = size_t(4) << 18;              // u32 per tile, P <= 2^18
-constexpr size_t kStateBytes = kCounterBytes + 256 * 8 + 256;  // + argmax keys + done counter
+constexpr size_t kKeyBytes = size_t(8) * kKeyCopies * kKeyRows * kKeyStride;  // argmax keys
+constexpr size_t kStateBytes = kCounterBytes + kKeyBytes + 256;                 // + done counter
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
@@ -1366,7 +1384,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   // sums where a later call expects zeroed counters.
   pl.off_cnt = 0;
   pl.off_keys = kCounterBytes;
-  pl.off_done = kCounterBytes + 256 * 8;
+  pl.off_done = kCounterBytes + kKeyBytes;
   pl.off_part = kStateBytes;
   const size_t part_bytes = (size_t)2 * G * m * tc * 4;
   pl.off_xf = (pl.off_part + part_bytes + 255) & ~size_t(255);

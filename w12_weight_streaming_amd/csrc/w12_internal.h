@@ -39,7 +39,7 @@ struct GemmParams {
   uint4* xf;              // x rearranged into MFMA B fragments (m >= 16)
   float* part;            // [2G][M][tile channels] split-tile partial sums
   uint32_t* tile_cnt;     // [P] arrival counters, zero between calls
-  unsigned long long* keys;  // [M] argmax keys, zero between calls
+  unsigned long long* keys;  // argmax keys: 8 copies x 256 rows x 16 u64 (one line per row), zero between calls
   uint32_t* done;         // [1] finished-workgroup counter, zero between calls
   int32_t* idx;
   float* maxval;
