@@ -22,7 +22,7 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and return as soon as the kernels are enqueued.
  *   - Argument errors return W12_EINVAL before anything is launched (null
- *     pointers, shapes the format cannot hold, m outside [1, 256], bf16
+ *     pointers, shapes the format cannot hold, m outside [1, 512], bf16
  *     matrices / records / x / y not 16-byte aligned, e_top and u32 arrays
  *     not 4-byte aligned); a
  *     workspace smaller than its query returns W12_ENOSPC; a failed launch
@@ -140,7 +140,7 @@ w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
  * m >= 16 bf16 MFMA (more than 192 rows run as several launches of at most
  * 192 rows, each streaming W again). The reduction over k is split across workgroups in a
  * fixed order (stream-K), so results are bitwise reproducible.
- *   x   [m, k] bf16 row-major, 1 <= m <= 256.
+ *   x   [m, k] bf16 row-major, 1 <= m <= 512.
  *   y   [m, n] row-major, fp32 (W12_Y_F32) or bf16 (W12_Y_BF16, the
  *       round-to-nearest-even of the same fp32 result).
  *   ws  zero-filled workspace of >= w12_gemm_workspace bytes.

@@ -68,13 +68,13 @@ def test_invalid_arguments_rejected_before_launch(L):
         assert L.w12_gemm(ctypes.byref(d), fake, 4, fake, 0, fake, 1 << 20, null) == EINVAL
         assert L.w12_head_argmax(ctypes.byref(d), fake, 4, fake, null, fake, 1 << 20, null) == EINVAL
     ok = w.W12Matrix(64, 256, 0x1000, 0x1000, 0x1000, 0x1000)
-    for m in (0, 257, -3):
+    for m in (0, 513, -3):
         assert L.w12_gemm(ctypes.byref(ok), fake, m, fake, 0, fake, 1 << 20, null) == EINVAL
     assert L.w12_gemm(ctypes.byref(ok), fake, 4, fake, 7, fake, 1 << 20, null) == EINVAL
     assert L.w12_gemm(ctypes.byref(ok), null, 4, fake, 0, fake, 1 << 20, null) == EINVAL
     sz = ctypes.c_size_t(0)
     assert L.w12_gemm_workspace(64, 257, 4, ctypes.byref(sz)) == EINVAL
-    assert L.w12_gemm_workspace(64, 256, 300, ctypes.byref(sz)) == EINVAL
+    assert L.w12_gemm_workspace(64, 256, 513, ctypes.byref(sz)) == EINVAL
     assert L.tree_accept(-1, fake, 0, fake, fake, fake, fake, fake, fake, null) == EINVAL
     assert L.tree_accept(2, null, 4, fake, fake, fake, fake, fake, fake, null) == EINVAL
     assert L.tree_accept(0, null, 0, null, null, null, null, null, null, null) == w.W12_OK

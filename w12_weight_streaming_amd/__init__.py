@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libw12.so")
 W12_OK, W12_EINVAL, W12_ENOSPC, W12_EHIP = 0, -1, -2, -3
 W12_Y_F32, W12_Y_BF16 = 0, 1
 MFMA_MIN_ROWS = 16
-MAX_ROWS = 256
+MAX_ROWS = 512
 
 _lib = None
 

@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int64_t kMaxK = int64_t(1) << 20;
-constexpr int64_t kMaxRows = 256;
+constexpr int64_t kMaxRows = 512;
 
 bool shape_ok(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0 || n % 32 != 0 || k % 256 != 0 || k > kMaxK) return false;
