@@ -135,7 +135,7 @@ def test_check_detects_corruption(w12):
 # ----------------------------------------------------------------------------- GEMM
 
 GEMM_SHAPES = [(1024, 1024), (96, 768), (320, 1792)]
-ROWS = [1, 2, 3, 5, 8, 15, 16, 17, 32, 33, 64, 100, 192, 256, 384, 512]
+ROWS = [1, 2, 3, 5, 8, 9, 12, 13, 15, 16, 17, 32, 33, 64, 100, 192, 256, 384, 512]
 
 
 @pytest.fixture(scope="module")
@@ -264,7 +264,7 @@ def check_argmax(idx, ref_idx, cands):
     return near
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 32, 48, 100, 192, 256, 512])
+@pytest.mark.parametrize("m", [1, 5, 12, 15, 16, 32, 48, 100, 192, 256, 512])
 def test_head_argmax(w12, m):
     n, k = 8192, 1024
     bits = synth.bits_u16(gen(n, k, 41, p_zero=0.01, p_outlier=0.001))

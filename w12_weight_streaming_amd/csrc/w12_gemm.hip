@@ -813,6 +813,10 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // 1 KB LDS buffer, from which the half-waves read their rows as broadcasts.
   constexpr bool kXLds = MV > 2;
   constexpr int XQ = kXLds ? 1 : MV;
+  // 16 rows of accumulators and a ring two units deep do not fit the register
+  // file (the kernel spilled to scratch and ran 13-15 rows at ~170 us on
+  // Wgate|Wup, twice the time at 12 rows); one unit deep they nearly do.
+  constexpr int kValuDepth = MV > 12 ? 1 : kDepth;
   __shared__ __align__(16) float lds[kLdsFloats];
   __shared__ __align__(16) char xlds[kXLds ? kNW * 1024 : 16];
   __shared__ int s_last;
@@ -934,7 +938,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   };
 
   if (u0 < u1) {
-    walk_slice<XQ, 2, kDepth>(L, u0, u1, issue_x, step);
+    walk_slice<XQ, 2, kValuDepth>(L, u0, u1, issue_x, step);
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax) {
@@ -1346,12 +1350,12 @@ KernelSel select_kernel(int M) {
     if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 2>), 1, kNT};
     return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP, 2>), 2, kNT};
   }
-  const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 12 ? 12 : 16;
   switch (mv) {
 #define W12_VALU(MV) \
   case MV:           \
     return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI, QP>), 0, kNT};
-    W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(16)
+    W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(12) W12_VALU(16)
 #undef W12_VALU
     default:
       return {nullptr, 0, 0};
