@@ -111,20 +111,28 @@ __global__ __launch_bounds__(64) void tree_search_kernel(const float* __restrict
 
   // rank the K children of every (position, parent slot): count the children
   // ahead of each one (higher score, or equal score and lower index)
-  for (int row = lane; row < D * K; row += 64) {
-    const float* v = L + (size_t)row * K;
-    float x[kMaxK];
+  // (a lane's rows are loaded before any is ranked, so their loads overlap)
+  constexpr int kRowsPerLane = kMaxD * kMaxK / 64;
+  float xr[kRowsPerLane][kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) x[j] = j < K ? v[j] : 0.f;
+  for (int t = 0; t < kRowsPerLane; ++t) {
+    const int row = lane + 64 * t;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) xr[t][j] = (row < D * K && j < K) ? L[(size_t)row * K + j] : 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < kRowsPerLane; ++t) {
+    const int row = lane + 64 * t;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      if (j >= K) break;
-      int rank = 0;
+      if (row < D * K && j < K) {
+        int rank = 0;
 #pragma unroll
-      for (int q = 0; q < kMaxK; ++q)
-        rank += (q < K && (x[q] > x[j] || (x[q] == x[j] && q < j))) ? 1 : 0;
-      s_lp[row * kMaxK + rank] = x[j];
-      s_slot[row * kMaxK + rank] = (uint8_t)j;
+        for (int q = 0; q < kMaxK; ++q)
+          rank += (q < K && (xr[t][q] > xr[t][j] || (xr[t][q] == xr[t][j] && q < j))) ? 1 : 0;
+        s_lp[row * kMaxK + rank] = xr[t][j];
+        s_slot[row * kMaxK + rank] = (uint8_t)j;
+      }
     }
   }
   __syncthreads();
@@ -231,6 +239,7 @@ __device__ __forceinline__ uint64_t global_key(float score, uint32_t depth, int 
 
 constexpr int kSelThreads = 512;
 constexpr int kSelMaxKeys = 8192;
+constexpr int kSelPerThread = kSelMaxKeys / kSelThreads;  // list entries per thread
 
 __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
     const ListEntry* __restrict__ lists, const int32_t* __restrict__ counts, int R, int cap,
@@ -242,28 +251,39 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
   __shared__ uint32_t s_sel;
   __shared__ int s_kk;
   __shared__ int s_total;
+  __shared__ int s_cnt[128];
   __shared__ int s_take[128];
   __shared__ int s_off[129];
 
   const int tid = threadIdx.x;
   const int n = R * cap;  // cap = 0: roots only, no lists
-  int np = 1;             // sort length: a power of two >= n
+  int np = 1;             // keys held: a power of two >= n
   while (np < n) np <<= 1;
-  for (int e = tid; e < np; e += kSelThreads) {
-    uint64_t key = ~0ull;  // past a list's end, and padding: sorts last
-    if (e < n) {
-      const int r = e / cap, i = e - r * cap;
-      if (i < counts[r]) {
-        const ListEntry le = lists[e];
-        key = global_key(le.score, (le.meta >> 16) & 31u, r, i);
-      }
-    }
-    s_key[e] = key;
-  }
   if (tid < 128) s_take[tid] = 0;
   if (tid == 0) s_total = 0;
+  if (tid < R) s_cnt[tid] = cap > 0 ? min(counts[tid], cap) : 0;
   __syncthreads();
-  if (tid < R && cap > 0) atomicAdd(&s_total, min(counts[tid], cap));
+  if (tid < R && cap > 0) atomicAdd(&s_total, s_cnt[tid]);
+  // this thread's list entries e = tid + j * kSelThreads, all loads issued
+  // before any is used (entries past a list's count are read but not used)
+  ListEntry le[kSelPerThread];
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {
+    const int e = tid + j * kSelThreads;
+    le[j] = e < n ? lists[e] : ListEntry{0.f, 0u, 0ull};
+  }
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {
+    const int e = tid + j * kSelThreads;
+    if (e < np) {
+      uint64_t key = ~0ull;  // past a list's end, and padding: sorts last
+      if (e < n) {
+        const int r = e / cap, i = e - r * cap;
+        if (i < s_cnt[r]) key = global_key(le[j].score, (le[j].meta >> 16) & 31u, r, i);
+      }
+      s_key[e] = key;
+    }
+  }
   __syncthreads();
   const int k = min(share, s_total);  // nodes kept
   // The k smallest keys are the kept nodes (keys are unique, and every list
@@ -358,16 +378,31 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
     if (node_depth) node_depth[row] = 0;
     if (score) score[row] = 0.f;
   }
-  for (int e = tid; e < n; e += kSelThreads) {
-    const int r = e / cap, i = e - r * cap;
-    if (i < s_take[r]) {
-      const ListEntry le = lists[e];
-      const int row = s_off[r] + 1 + i;
-      const uint32_t d = (le.meta >> 16) & 31u, slot = (le.meta >> 12) & 15u;
-      parent[row] = (int32_t)(le.meta & 0xFFFu);
-      token[row] = tok[((size_t)r * D + (d - 1)) * K + slot];
-      if (node_depth) node_depth[row] = (int32_t)d;
-      if (score) score[row] = le.score;
+  int32_t tk[kSelPerThread];
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {  // token loads first, all in flight together
+    const int e = tid + j * kSelThreads;
+    tk[j] = 0;
+    if (e < n) {
+      const int r = e / cap, i = e - r * cap;
+      if (i < s_take[r]) {
+        const uint32_t d = (le[j].meta >> 16) & 31u, slot = (le[j].meta >> 12) & 15u;
+        tk[j] = tok[((size_t)r * D + (d - 1)) * K + slot];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSelPerThread; ++j) {
+    const int e = tid + j * kSelThreads;
+    if (e < n) {
+      const int r = e / cap, i = e - r * cap;
+      if (i < s_take[r]) {
+        const int row = s_off[r] + 1 + i;
+        parent[row] = (int32_t)(le[j].meta & 0xFFFu);
+        token[row] = tk[j];
+        if (node_depth) node_depth[row] = (int32_t)((le[j].meta >> 16) & 31u);
+        if (score) score[row] = le[j].score;
+      }
     }
   }
 }
