@@ -45,10 +45,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources the verify GEMM kernels are built from: the counter traffic
+# stored with the profiles holds only while these are unchanged.
+GEMM_SOURCES = ("w12_gemm.hip", "w12_device.h", "w12_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w12_weight_streaming_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
