@@ -24,13 +24,18 @@
 //  * 16 <= m <= 64: bf16 MFMA 32x32x16, weights = A, x = B. The B fragments come
 //    from a copy of x rearranged once per call so that every fragment load
 //    is one contiguous 1 KB per wave (xfrag_kernel).
-//  * m < 16: lanes own channels, fdot2 against x rows read from memory
-//    (all lanes of a half-wave read the same 16 bytes).
+//  * m < 16: lanes own channels, fdot2 against x rows (up to 2 rows read
+//    from memory by every lane of a half-wave; more rows ride in the load
+//    ring and are broadcast through a per-wave LDS buffer).
 //  * Escapes (~1% of weights here): restored pairs go through a per-wave LDS
 //    buffer, the lanes holding the block's escape entries overwrite their
 //    slots, and the pairs are read back -- all synchronised within the wave.
-//  * Escape-block offsets and window tops are wave-uniform and come through
-//    the scalar data cache.
+//  * Escape-block offsets and window tops are read with vector loads in the
+//    same in-order streams as the records (every lane reads the block's two
+//    offsets; each lane reads the dword holding its channel's window top), so
+//    one wait count covers a unit's loads.
+//  * Argmax keys: one copy per XCD and one cache line per row; the last
+//    workgroup of the grid merges the copies.
 #include <atomic>
 #include <type_traits>
 #include <utility>
