@@ -63,8 +63,9 @@ def gemm_bytes(pw, m: int, out_bytes_per_elem: int) -> int:
     return pw.nbytes() + 2 * m * pw.k + out_bytes_per_elem * m * pw.n
 
 
-def build_block(w12, synth, torch, dev):
-    """Pack the block and head; returns dict name -> (PackedW12, x)."""
+def build_block(w12, synth, torch, dev, dense=None):
+    """Pack the block and head; returns dict name -> (PackedW12, x). With a
+    dict `dense`, the bf16 source weights are kept in it by name."""
     specs = [
         ("QKV", [(Q_OUT, HIDDEN, 1), (KV_OUT, HIDDEN, 2), (KV_OUT, HIDDEN, 3)]),
         ("O", [(HIDDEN, Q_OUT, 4)]),
@@ -88,6 +89,8 @@ def build_block(w12, synth, torch, dev):
         k = parts[0][1]
         x = synth.activations_bf16(M_ROWS, k, seed=1_000_000 * cfg + parts[0][2] + 500, device=dev)
         mats[name] = (pw, x)
+        if dense is not None:
+            dense[name] = w
         del w
         log(f"packed {name}: {pw.n}x{pw.k}, {pw.n_esc} escapes "
             f"({pw.n_esc / (pw.n * pw.k):.4%}), {8 * pw.nbytes() / (pw.n * pw.k):.4f} bits/weight")
@@ -100,6 +103,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense bf16 context timing of the same step")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
@@ -141,7 +146,8 @@ def main():
     if args.workload == "tree":
         return run_tree(args, w12, synth, torch, dev)
 
-    mats, pack_gbps = build_block(w12, synth, torch, dev)
+    dense = None if args.no_dense else {}
+    mats, pack_gbps = build_block(w12, synth, torch, dev, dense)
     order = ["QKV", "O", "UP", "DOWN"]
     outs = {n: torch.empty(M_ROWS, mats[n][0].n, dtype=torch.bfloat16, device=dev) for n in order}
     head_pw, head_x = mats["HEAD"]
@@ -254,6 +260,39 @@ def main():
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(per_launch)}
 
+    # context only: the same step on the dense bf16 weights through
+    # torch's GEMM (2-D products) and torch.argmax, timed the same way
+    dense_ctx = None
+    if dense is not None:
+        F = torch.nn.functional
+        ys = {n: torch.empty(M_ROWS, dense[n].shape[0], dtype=torch.bfloat16, device=dev) for n in order}
+
+        def dense_step():
+            for n in order:
+                torch.matmul(mats[n][1], dense[n].t(), out=ys[n])
+            return torch.argmax(F.linear(head_x, dense["HEAD"]).float(), dim=1)
+
+        for _ in range(args.warmup):
+            dense_step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            d_idx = dense_step()
+        b.record()
+        torch.cuda.synchronize()
+        d_ms = a.elapsed_time(b) / args.steps
+        d_bytes = sum(2 * dense[n].numel() + 2 * M_ROWS * dense[n].shape[1] + 2 * M_ROWS * dense[n].shape[0]
+                      for n in order) + 2 * dense["HEAD"].numel() + 2 * M_ROWS * HIDDEN
+        dense_ctx = {"what": "the block GEMMs and the head argmax on the bf16 source weights via torch.matmul "
+                             "and torch.argmax (no tree acceptance); context, not a baseline",
+                     "ms_per_step": round(d_ms, 4), "bytes_per_step": int(d_bytes),
+                     "GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                     "w12_step_speedup": round(d_ms / ms_per_step, 3),
+                     "head_argmax_agrees": float((d_idx == head_idx[0]).float().mean())}
+        del dense
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(mats, synth, torch)
@@ -287,6 +326,7 @@ def main():
         "accepted": {"accept_len": int(acc[0]), "bonus": int(bonus[0])},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "dense_bf16_context": dense_ctx,
     }
     print(json.dumps(line), flush=True)
 
