@@ -112,7 +112,7 @@ def main():
                     help="block: one 27B-class block + LM head at M=32 (the headline line); "
                          "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
                          "and 2%% outliers; stack: 64 blocks in sequence at M=32; "
-                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 192; "
+                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 512; "
                          "qpass: the block step through the Q pass (8-bit view only); "
                          "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree")
     args = ap.parse_args()
