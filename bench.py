@@ -242,7 +242,7 @@ def main():
     # roofline of the dominant kernel (most time per step)
     dominant = "HEAD" if kern_us["HEAD"] >= block_us else "BLOCK"
     if dominant == "HEAD":
-        ach, kname = head_gbps, ("gemm_mfma_kernel<1,1>: LM head 152064x5120 + fused argmax, M=32 "
+        ach, kname = head_gbps, ("gemm_mfma_kernel<1,1,false,4> (4-strip tiles): LM head 152064x5120 + fused argmax, M=32 "
                                  "(event time of the w12_head_argmax call, x pre-pass included)")
         per_launch = step_bytes["HEAD"]
     else:

@@ -474,3 +474,39 @@ def test_full_size_head_argmax(w12):
     del w
     ref_idx, _, cands = V.head_argmax(synth.bits_u16(x)[rows], wb, chunk=16384)
     check_argmax(host(idx)[rows], ref_idx, cands)
+
+
+def test_full_size_head_shape_four_strip_tiles(w12):
+    """At the LM-head shape (152064x5120) up to 32 rows run 4-strip tiles:
+    the GEMM (exact and Q pass) on sampled columns against the oracle, and
+    the fused argmax (exact and Q pass) against the argmax of those logits."""
+    n, k = 152064, 5120
+    w = gen(n, k, 4300, device=DEV)
+    pw = w12.w12_pack(w)
+    rng = np.random.default_rng(4301)
+    cols = np.sort(rng.choice(n, 64, replace=False))
+    wb_cols = synth.bits_u16(w[torch.as_tensor(cols, device=DEV)])
+    strips = rng.choice(n // 32, 2, replace=False)
+    qcols = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in strips])
+    wq = F.qpass_weights(F.pack(synth.bits_u16(w[torch.as_tensor(qcols, device=DEV)])), len(qcols), k)
+    del w
+    for m in (17, 32):
+        say("head shape, 4-strip tiles, m", m)
+        x = synth.activations_bf16(m, k, 4302 + m, device=DEV)
+        xb = synth.bits_u16(x)
+        y = host(w12.w12_gemm(pw, x))
+        y_ref, bound = V.gemm_ref(xb, wb_cols)
+        assert V.within_tolerance(y[:, cols], y_ref, bound).all(), m
+        idx, mx = w12.w12_head_argmax(pw, x)
+        idx = host(idx)
+        # the fused argmax is the argmax of the same logits (lowest id on ties)
+        assert np.array_equal(idx, np.argmax(y, axis=1)), m
+        assert np.array_equal(host(mx), y[np.arange(m), idx]), m
+    m = 32
+    x = synth.activations_bf16(m, k, 4340, device=DEV)
+    yq = host(w12.w12_gemm(pw, x, qpass=True))
+    yq_ref, bound = V.gemm_ref(synth.bits_u16(x), wq)
+    assert V.within_tolerance(yq[:, qcols], yq_ref, bound).all()
+    iq, mq = w12.w12_head_argmax(pw, x, qpass=True)
+    assert np.array_equal(host(iq), np.argmax(yq, axis=1))
+    assert np.array_equal(host(mq), yq[np.arange(m), host(iq)])

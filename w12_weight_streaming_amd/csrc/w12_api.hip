@@ -93,6 +93,7 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
     p.P = pl.P;
     p.U = pl.U;
     p.G = pl.G;
+    p.nq = pl.nq;
     p.y = y ? static_cast<void*>(static_cast<char*>(y) + m0 * y_row) : nullptr;
     p.ytype = ytype;
     p.part = reinterpret_cast<float*>(base + pl.off_part);

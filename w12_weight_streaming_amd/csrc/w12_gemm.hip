@@ -671,8 +671,8 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   static_assert(MT >= 1 && MT <= 2, "small-m kernel: at most 64 rows");
   constexpr int XQ = MT;
   // NQ strips per tile (each x load serves NQ strips). With 4 strips the ring
-  // is one unit deep to stay within the register file; measured at 32 rows
-  // that was slower than 2 strips two units deep, which is the one selected.
+  // is one unit deep to stay within the register file; the plan picks 4-strip
+  // tiles (up to 32 rows) only where slices hold many units.
   constexpr int D = NQ == 4 ? 1 : 2;
   constexpr int TC = NQ * kStrip;       // channels per tile
   constexpr int RS = TC + 4;            // reduction slot row stride (floats)
@@ -1338,8 +1338,13 @@ struct KernelSel {
   int threads;  // workgroup size
 };
 
+// Units per slice (at 4 strips per tile) from which m <= 32 uses 4-strip
+// tiles. Measured at 32 rows: the 152064x5120 LM head (93 units per slice)
+// 3% faster with 4 strips, Wgate|Wup 34816x5120 (21) 5% slower.
+constexpr int kNq4MinUnits = 48;
+
 template <int EPI, bool QP>
-KernelSel select_kernel(int M) {
+KernelSel select_kernel(int M, int nq) {
   if (M > kSmallMaxRows) {
     switch ((M + 31) / 32) {
 #define W12_BIG(MT) \
@@ -1352,7 +1357,9 @@ KernelSel select_kernel(int M) {
     }
   }
   if (M >= 16) {
-    if (M <= 32) return {reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 2>), 1, kNT};
+    if (M <= 32)
+      return nq == 4 ? KernelSel{reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 4>), 1, kNT}
+                     : KernelSel{reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 2>), 1, kNT};
     return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP, 2>), 2, kNT};
   }
   const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 12 ? 12 : 16;
@@ -1376,8 +1383,18 @@ constexpr size_t kStateBytes = kCounterBytes + kKeyBytes + 256;                 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   GemmPlan pl{};
   const bool big = m > kSmallMaxRows;
-  const int64_t tc = big ? kBigTC : 2 * kStrip;  // channels per tile of the kernel select_kernel picks
-  const int64_t S = n / kStrip, sp = tc / kStrip, P = (S + sp - 1) / sp, RK = k / kRecK;
+  const int64_t S = n / kStrip, RK = k / kRecK;
+  // Up to 32 rows, tiles of 4 strips when the slices stay long (each x
+  // fragment then serves 4 strips, and tiles end half as often); shorter
+  // slices keep 2-strip tiles, whose finer units balance the slices better.
+  int nq = 2;
+  if (!big && m >= 16 && m <= 32) {
+    const int64_t U4 = ((S + 3) / 4) * RK;
+    const int64_t G4 = U4 < num_cu ? U4 : num_cu;
+    if (U4 >= (int64_t)kNq4MinUnits * G4) nq = 4;
+  }
+  const int64_t tc = big ? kBigTC : nq * kStrip;  // channels per tile of the kernel select_kernel picks
+  const int64_t sp = tc / kStrip, P = (S + sp - 1) / sp;
   const int64_t mt = (!big && m >= 16) ? (m + 31) / 32 : 0;
   const int64_t U = P * RK;
   // one workgroup per compute unit, every slice resident at once
@@ -1387,6 +1404,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   pl.G = (int)G;
   pl.U = (int)U;
   pl.P = (int)P;
+  pl.nq = nq;
   // The counter region has the same place and size for every shape (any
   // shape's tile counters, the argmax keys and the done counter), so a
   // workspace shared by calls of different shapes never holds old partial
@@ -1402,8 +1420,8 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s) {
-  const KernelSel k = qpass ? (epi == kEpiY ? select_kernel<kEpiY, true>(p.M) : select_kernel<kEpiArgmax, true>(p.M))
-                            : (epi == kEpiY ? select_kernel<kEpiY, false>(p.M) : select_kernel<kEpiArgmax, false>(p.M));
+  const KernelSel k = qpass ? (epi == kEpiY ? select_kernel<kEpiY, true>(p.M, p.nq) : select_kernel<kEpiArgmax, true>(p.M, p.nq))
+                            : (epi == kEpiY ? select_kernel<kEpiY, false>(p.M, p.nq) : select_kernel<kEpiArgmax, false>(p.M, p.nq));
   if (!k.fn) return hipErrorInvalidValue;
   if (k.mt > 0) {
     const int64_t chunks = (int64_t)(p.K / 32) * k.mt * 128;

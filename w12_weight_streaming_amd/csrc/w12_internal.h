@@ -34,6 +34,7 @@ struct GemmParams {
   int P;   // tiles = ceil(S / strips per tile)
   int U;   // units = P * RK
   int G;   // workgroups
+  int nq;  // strips per tile of the small-m MFMA kernel (from the plan)
   void* y;
   int ytype;
   uint4* xf;              // x rearranged into MFMA B fragments (m >= 16)
@@ -47,6 +48,7 @@ struct GemmParams {
 
 struct GemmPlan {
   int G, U, P;
+  int nq;  // strips per tile of the small-m MFMA kernel (2 or 4)
   size_t ws_bytes;
   size_t off_cnt, off_part, off_keys, off_done, off_xf;
 };
