@@ -120,7 +120,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the verify path is single-GPU here, see DESIGN.md for how it would shard.",
+              "the verify path runs on one GPU here; across GPUs the weights would shard by "
+              "32-channel strips (column-parallel layers, the LM head) or 256-column records (row-parallel ones).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -9,7 +9,7 @@ What the pages fix ([S1] section 4.1, [S2] W12 paragraph):
   * a record is 12 KB: the first 8 KB is the 8-bit view, the last 4 KB the
     low mantissa bits; restored tensors equal the source bit-for-bit.
 
-Readings taken where the pages are open (each also listed in the design doc):
+Readings taken where the pages are open:
   R1  E_n maximises the number of in-window weights; the smallest such E_n
       wins a tie; E_n in [16, 254] so the window holds normal exponents only.
   R2  8-bit view byte hi8 = s<<7 | o<<3 | m>>4 (sign, offset, top three
