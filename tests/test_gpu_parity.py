@@ -510,3 +510,25 @@ def test_full_size_head_shape_four_strip_tiles(w12):
     iq, mq = w12.w12_head_argmax(pw, x, qpass=True)
     assert np.array_equal(host(iq), np.argmax(yq, axis=1))
     assert np.array_equal(host(mq), yq[np.arange(m), host(iq)])
+
+
+def test_four_strip_tiles_with_a_partial_last_tile(w12):
+    """2461 strips x 20 records: 4-strip tiles on a 256-CU device (12320
+    units), the last tile holding one strip. Sampled columns include that
+    strip; the fused argmax must equal the argmax of the logits."""
+    n, k, m = 2461 * 32, 5120, 32
+    w = gen(n, k, 4400, device=DEV)
+    pw = w12.w12_pack(w)
+    rng = np.random.default_rng(4401)
+    cols = np.sort(np.concatenate([rng.choice(n - 32, 48, replace=False), np.arange(n - 32, n)]))
+    wb = synth.bits_u16(w[torch.as_tensor(cols, device=DEV)])
+    del w
+    x = synth.activations_bf16(m, k, 4402, device=DEV)
+    y = host(w12.w12_gemm(pw, x))
+    y_ref, bound = V.gemm_ref(synth.bits_u16(x), wb)
+    assert V.within_tolerance(y[:, cols], y_ref, bound).all()
+    idx, mx = w12.w12_head_argmax(pw, x)
+    idx = host(idx)
+    assert idx.max() < n
+    assert np.array_equal(idx, np.argmax(y, axis=1))
+    assert np.array_equal(host(mx), y[np.arange(m), idx])
