@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
-"""Benchmark: one W12 verify pass of a 27B-class transformer block at M=32
-tree-node rows, on one MI355X.
+"""Benchmark: one W12 verify pass of a 64-layer 27B-class stack at M=32
+tree-node rows, then the LM-head argmax and tree acceptance, on one MI355X.
 
 A step is one pass of the whole verify hot path over resident inputs:
-  QKV   [Wq;Wk;Wv]   8192 x 5120   (Wq 6144x5120, Wk/Wv 1024x5120, fused:
-                                    they share their input rows)
-  O     Wo           5120 x 6144
-  UP    [Wgate;Wup] 34816 x 5120   (fused, shared input)
-  DOWN  Wdown        5120 x 17408
+  64 layers, each
+    QKV   [Wq;Wk;Wv]   8192 x 5120   (Wq 6144x5120, Wk/Wv 1024x5120, fused:
+                                      they share their input rows)
+    O     Wo           5120 x 6144
+    UP    [Wgate;Wup] 34816 x 5120   (fused, shared input)
+    DOWN  Wdown        5120 x 17408
   HEAD  LM head    152064 x 5120 + fused argmax per row
   TREE  greedy acceptance of one 32-node draft tree
-Weights are seeded synthetic bf16 (N(0, 0.02) x per-channel lognormal(0, 0.5)
-scale, 1% zeros, 0.1% x64 outliers), packed to W12 and checked bit-for-bit
-before timing; activations are seeded N(0, 1) bf16 rows.
+Every layer has its own seeded synthetic weights (N(0, 0.02) x per-channel
+lognormal(0, 0.5) scale, 1% zeros, 0.1% x64 outliers), packed to W12 and
+checked bit-for-bit before timing (about 34 GB of W12 resident in HBM), and
+its own seeded N(0, 1) bf16 input rows, so nothing is served from the caches
+between layers.
 
 value = algorithmic bytes of a step / step time. Algorithmic bytes of a
 W12 GEMM = records 1.5NK + e_top N + esc_off 4(NK/1024+1) + escapes
@@ -37,8 +40,17 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 M_ROWS = 32
+LAYERS = 64
 HIDDEN, Q_OUT, KV_OUT, FFN, VOCAB = 5120, 6144, 1024, 17408, 152064
 METRIC = "W12 verify-GEMM effective HBM GB/s at M=32 rows; % of MI355X HBM peak"
+# (name, out channels, in channels) of one layer's four W12 GEMMs
+LAYER_SHAPES = (("QKV", Q_OUT + 2 * KV_OUT, HIDDEN), ("O", HIDDEN, Q_OUT),
+                ("UP", 2 * FFN, HIDDEN), ("DOWN", HIDDEN, FFN))
+# kernel each call type runs at M=32 (the plan picks 2-strip tiles for the
+# block shapes and 4-strip tiles for the head)
+KERNEL_OF = {"QKV": "gemm_mfma_kernel<1, 0, false, 2>", "O": "gemm_mfma_kernel<1, 0, false, 2>",
+             "UP": "gemm_mfma_kernel<1, 0, false, 2>", "DOWN": "gemm_mfma_kernel<1, 0, false, 2>",
+             "HEAD": "gemm_mfma_kernel<1, 1, false, 4>", "TREE": "tree_accept_kernel"}
 
 
 def log(*a):
@@ -63,128 +75,121 @@ def gemm_bytes(pw, m: int, out_bytes_per_elem: int) -> int:
     return pw.nbytes() + 2 * m * pw.k + out_bytes_per_elem * m * pw.n
 
 
-def build_block(w12, synth, torch, dev, dense=None):
-    """Pack the block and head; returns dict name -> (PackedW12, x). With a
-    dict `dense`, the bf16 source weights are kept in it by name."""
-    specs = [
-        ("QKV", [(Q_OUT, HIDDEN, 1), (KV_OUT, HIDDEN, 2), (KV_OUT, HIDDEN, 3)]),
-        ("O", [(HIDDEN, Q_OUT, 4)]),
-        ("UP", [(FFN, HIDDEN, 5), (FFN, HIDDEN, 6)]),
-        ("DOWN", [(HIDDEN, FFN, 7)]),
-        ("HEAD", [(VOCAB, HIDDEN, 8)]),
-    ]
-    mats, pack_s, pack_in = {}, 0.0, 0
-    for name, parts in specs:
-        # seed = 1,000,000 * config + 1000 * layer + matrix (config 2, layer 0;
-        # the head is config 4)
-        cfg = 4 if name == "HEAD" else 2
-        w = torch.cat([synth.weights_bf16(n, k, seed=1_000_000 * cfg + idx, device=dev)
-                       for (n, k, idx) in parts], dim=0)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        pw = w12.w12_pack(w, check=True)       # raises unless bit-exact
-        torch.cuda.synchronize()
-        pack_s += time.perf_counter() - t0
-        pack_in += w.numel() * 2
-        k = parts[0][1]
-        x = synth.activations_bf16(M_ROWS, k, seed=1_000_000 * cfg + parts[0][2] + 500, device=dev)
-        mats[name] = (pw, x)
-        if dense is not None:
-            dense[name] = w
-        del w
-        log(f"packed {name}: {pw.n}x{pw.k}, {pw.n_esc} escapes "
-            f"({pw.n_esc / (pw.n * pw.k):.4%}), {8 * pw.nbytes() / (pw.n * pw.k):.4f} bits/weight")
-    return mats, pack_in / pack_s / 1e9
+def head_bytes(pw, m: int) -> int:
+    return pw.nbytes() + 2 * m * pw.k + 4 * m
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true",
-                    help="skip the dense bf16 context timing of the same step")
-    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
-    ap.add_argument("--copy-gib", type=float, default=1.0,
-                    help="size of the calibration copy launched after timing (0 = none)")
-    ap.add_argument("--workload", choices=("block", "batched", "stack", "sweep", "qpass", "tree"), default="block",
-                    help="block: one 27B-class block + LM head at M=32 (the headline line); "
-                         "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
-                         "and 2%% outliers; stack: 64 blocks in sequence at M=32; "
-                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 512; "
-                         "qpass: the block step through the Q pass (8-bit view only); "
-                         "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree")
-    args = ap.parse_args()
+def tree_bytes(m: int) -> int:
+    return 4 * (2 + 3 * m) + 4 * (2 + m)
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the verify path runs on one GPU here; across GPUs the weights would shard by "
-              "32-channel strips (column-parallel layers, the LM head) or 256-column records (row-parallel ones).",
-              file=sys.stderr)
-        sys.exit(2)
 
+def traffic_for(name: str):
+    """Counter-measured HBM bytes per launch of a call type, if the stored
+    counters were taken on the current kernel sources."""
+    tfile = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(tfile):
+        return None
+    with open(tfile) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("per_launch_bytes", {}).get(name)
+
+
+def pack_layers(w12, synth, torch, dev, layers, keep_dense=False):
+    """W12-pack `layers` layers of the 27B-class shape (seed 3,000,000 +
+    1000 * layer + matrix) with the load-time check; each GEMM gets its own
+    input rows (seed + 500). Returns ([{name: (PackedW12, x)}], dense or
+    None, pack GB/s of bf16 input)."""
+    mats, dense = [], ([] if keep_dense else None)
+    pack_s, pack_in = 0.0, 0
+    for li in range(layers):
+        row, drow = {}, {}
+        for j, (name, n, k) in enumerate(LAYER_SHAPES):
+            seed = 1_000_000 * 3 + 1000 * li + j + 1
+            w = synth.weights_bf16(n, k, seed=seed, device=dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            pw = w12.w12_pack(w, check=True)       # raises W12_ECORRUPT unless bit-exact
+            torch.cuda.synchronize()
+            pack_s += time.perf_counter() - t0
+            pack_in += w.numel() * 2
+            x = synth.activations_bf16(M_ROWS, k, seed=seed + 500, device=dev)
+            row[name] = (pw, x)
+            if keep_dense:
+                drow[name] = w
+            del w
+        mats.append(row)
+        if keep_dense:
+            dense.append(drow)
+        if li % 16 == 15 or li == layers - 1:
+            log(f"packed {li + 1} layers")
+    return mats, dense, pack_in / max(pack_s, 1e-9) / 1e9
+
+
+def pack_head(w12, synth, torch, dev, keep_dense=False):
+    """The 152064x5120 LM head (seed 4,000,008), its 32 input rows, and the
+    top-16 candidate ids of every row (drawn with torch from the bf16
+    source weights: synthetic input for the draft tree, outside any timed
+    region)."""
+    w = synth.weights_bf16(VOCAB, HIDDEN, seed=1_000_000 * 4 + 8, device=dev)
+    pw = w12.w12_pack(w, check=True)
+    x = synth.activations_bf16(M_ROWS, HIDDEN, seed=1_000_000 * 4 + 508, device=dev)
+    logits = torch.cat([x.float() @ w[v0:v0 + 16384].float().t() for v0 in range(0, VOCAB, 16384)], dim=1)
+    top16 = torch.topk(logits, 16, dim=1).indices.cpu().numpy()
+    del logits
+    log(f"packed HEAD: {pw.n}x{pw.k}, {pw.n_esc} escapes ({pw.n_esc / (pw.n * pw.k):.4%}), "
+        f"{8 * pw.nbytes() / (pw.n * pw.k):.4f} bits/weight")
+    return pw, x, top16, (w if keep_dense else None)
+
+
+def run_pass(args, w12, synth, torch, dev):
+    """The headline: 64 layers + LM head argmax + tree acceptance at M=32."""
     import numpy as np
-    import torch
 
-    import synth
-    import w12_weight_streaming_amd as w12
+    layers = args.layers
+    keep_dense = not args.no_dense
+    mats, dense, pack_gbps = pack_layers(w12, synth, torch, dev, layers, keep_dense)
+    head_pw, head_x, top16, head_dense = pack_head(w12, synth, torch, dev, keep_dense)
+    outs = {name: torch.empty(M_ROWS, n, dtype=torch.bfloat16, device=dev) for name, n, _ in LAYER_SHAPES}
+    ws = w12.workspace(max([w12.gemm_workspace_bytes(n, k, M_ROWS) for _, n, k in LAYER_SHAPES] +
+                           [w12.gemm_workspace_bytes(head_pw.n, head_pw.k, M_ROWS)]), dev)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w12.lib()
-
-    if args.workload == "batched":
-        return run_batched(args, w12, synth, torch, dev)
-    if args.workload == "stack":
-        return run_stack(args, w12, synth, torch, dev)
-    if args.workload == "sweep":
-        return run_sweep(args, w12, synth, torch, dev)
-    if args.workload == "qpass":
-        return run_qpass(args, w12, synth, torch, dev)
-    if args.workload == "tree":
-        return run_tree(args, w12, synth, torch, dev)
-
-    dense = None if args.no_dense else {}
-    mats, pack_gbps = build_block(w12, synth, torch, dev, dense)
-    order = ["QKV", "O", "UP", "DOWN"]
-    outs = {n: torch.empty(M_ROWS, mats[n][0].n, dtype=torch.bfloat16, device=dev) for n in order}
-    head_pw, head_x = mats["HEAD"]
-    ws = w12.workspace(max(w12.gemm_workspace_bytes(mats[n][0].n, mats[n][0].k, M_ROWS)
-                           for n in order + ["HEAD"]), dev)
-
-    # tree inputs: one 32-node tree over the verify rows (config 4 shape:
-    # depth <= 16, a node's token equals its parent row's argmax w.p. 0.7)
+    # tree inputs: one 32-node tree over the head's rows (depth <= 16; a
+    # node's token equals its parent row's argmax w.p. 0.7, else another of
+    # that row's top-16 candidates)
     idx0, _ = w12.w12_head_argmax(head_pw, head_x, ws=ws, with_max=False)
     am = idx0.cpu().numpy().astype(np.int32)
-    parent, token = synth.random_tree(M_ROWS, 16, am, None, 0.7, seed=4_000_000 + 9, vocab=VOCAB)
+    parent, token = synth.random_tree(M_ROWS, 16, am, top16, 0.7, seed=4_000_000 + 9, vocab=VOCAB)
     t_off = torch.tensor([0, M_ROWS], dtype=torch.int32, device=dev)
     t_par = torch.tensor(parent, dtype=torch.int32, device=dev)
     t_tok = torch.tensor(token, dtype=torch.int32, device=dev)
-
-    def launch(name):
-        if name == "HEAD":
-            return w12.w12_head_argmax(head_pw, head_x, ws=ws, with_max=False)[0]
-        if name == "TREE":
-            return w12.tree_accept(t_off, t_par, t_tok, head_idx[0])
-        pw, x = mats[name]
-        return w12.w12_gemm(pw, x, out=outs[name], ws=ws)
-
     head_idx = [idx0]
 
+    def launch(name, li=0):
+        if name == "HEAD":
+            head_idx[0] = w12.w12_head_argmax(head_pw, head_x, ws=ws, with_max=False)[0]
+            return
+        if name == "TREE":
+            return w12.tree_accept(t_off, t_par, t_tok, head_idx[0])
+        pw, x = mats[li][name]
+        w12.w12_gemm(pw, x, out=outs[name], ws=ws)
+
+    order = [name for name, _, _ in LAYER_SHAPES]
+
     def step():
-        for n in order:
-            launch(n)
-        head_idx[0] = launch("HEAD")
+        for li in range(layers):
+            for name in order:
+                launch(name, li)
+        launch("HEAD")
         launch("TREE")
 
-    names = order + ["HEAD", "TREE"]
-    step_bytes = {n: gemm_bytes(mats[n][0], M_ROWS, 2) for n in order}
-    step_bytes["HEAD"] = head_pw.nbytes() + 2 * M_ROWS * HIDDEN + 4 * M_ROWS
-    step_bytes["TREE"] = 4 * (2 + 3 * M_ROWS) + 4 * (2 + M_ROWS)
+    step_bytes = {name: sum(gemm_bytes(row[name][0], M_ROWS, 2) for row in mats) for name in order}
+    step_bytes["HEAD"] = head_bytes(head_pw, M_ROWS)
+    step_bytes["TREE"] = tree_bytes(M_ROWS)
     total_bytes = sum(step_bytes.values())
+    calls = {name: layers for name in order}
+    calls.update({"HEAD": 1, "TREE": 1})
 
     graph = None
     if args.graph:
@@ -193,7 +198,6 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
-
     run = graph.replay if graph is not None else step
     for _ in range(args.warmup):
         run()
@@ -206,25 +210,35 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # correctness of what was timed: the accepted path is a valid greedy path
+    # the accepted path of what was timed
     acc, path, bonus = w12.tree_accept(t_off, t_par, t_tok, head_idx[0])
     torch.cuda.synchronize()
 
-    # per-kernel durations, measured with events on the launch stream inside
-    # full passes (so every launch streams its weights from HBM)
-    reps = max(5, min(args.steps, 20))
-    ev = {n: [] for n in names}
+    # per-call durations: the same steps again with a pair of events around
+    # every call, recorded on the stream the kernels run on (every launch
+    # still streams its weights from HBM: 34 GB per step)
+    reps = max(2, min(args.steps, 5))
+    ev = {n: [] for n in order + ["HEAD", "TREE"]}
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
     for _ in range(reps):
-        for n in names:
+        for li in range(layers):
+            for name in order:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                launch(name, li)
+                b.record()
+                ev[name].append((a, b))
+        for name in ("HEAD", "TREE"):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            r = launch(n)
-            if n == "HEAD":
-                head_idx[0] = r
+            launch(name)
             b.record()
-            ev[n].append((a, b))
+            ev[name].append((a, b))
+    a1.record()
     torch.cuda.synchronize()
-    kern_us = {n: 1000.0 * sum(a.elapsed_time(b) for a, b in ev[n]) / reps for n in names}
+    instrumented_ms = a0.elapsed_time(a1) / reps
+    call_us = {n: 1000.0 * sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in ev.items()}
 
     if args.copy_gib > 0:  # plain copy of known size, the HBM-counter calibration reference
         nb = int(args.copy_gib * (1 << 30))
@@ -234,69 +248,33 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    block_us = sum(kern_us[n] for n in order)
-    block_bytes = sum(step_bytes[n] for n in order)
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
-    block_gbps = block_bytes / (block_us * 1e-6) / 1e9
-    head_gbps = step_bytes["HEAD"] / (kern_us["HEAD"] * 1e-6) / 1e9
+    per_step_us = {n: call_us[n] * calls[n] for n in call_us}
+    block_us = sum(per_step_us[n] for n in order)
+    block_bytes = sum(step_bytes[n] for n in order)
+    gbps_of = {n: step_bytes[n] / calls[n] / (call_us[n] * 1e-6) / 1e9 for n in call_us}
 
-    # roofline of the dominant kernel (most time per step)
-    dominant = "HEAD" if kern_us["HEAD"] >= block_us else "BLOCK"
-    if dominant == "HEAD":
-        ach, kname = head_gbps, ("gemm_mfma_kernel<1,1,false,4> (4-strip tiles): LM head 152064x5120 + fused argmax, M=32 "
-                                 "(event time of the w12_head_argmax call, x pre-pass included)")
-        per_launch = step_bytes["HEAD"]
-    else:
-        ach, kname = block_gbps, ("gemm_mfma_kernel<1,0>: block GEMMs at M=32 "
-                                  "(event time of the w12_gemm calls, x pre-pass included)")
-        per_launch = block_bytes / len(order)
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            t = json.load(f)
-        if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("per_launch_bytes", {}).get(dominant)
-    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": int(per_launch)}
+    # roofline of the dominant kernel: the call type with the most time per step
+    dominant = max(order + ["HEAD"], key=lambda n: per_step_us[n])
+    per_launch = step_bytes[dominant] // calls[dominant]
+    roofline = {"bound": "hbm",
+                "kernel": f"{KERNEL_OF[dominant]}: {dominant} at M=32, {calls[dominant]} launches per step "
+                          "(event time per call on the launch stream, every kernel of the call included)",
+                "achieved": round(gbps_of[dominant], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps_of[dominant] / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dominant),
+                "algorithmic_bytes_per_launch": int(per_launch),
+                "avg_launch_us": round(call_us[dominant], 2)}
 
-    # context only: the same step on the dense bf16 weights through
-    # torch's GEMM (2-D products) and torch.argmax, timed the same way
     dense_ctx = None
-    if dense is not None:
-        F = torch.nn.functional
-        ys = {n: torch.empty(M_ROWS, dense[n].shape[0], dtype=torch.bfloat16, device=dev) for n in order}
-
-        def dense_step():
-            for n in order:
-                torch.matmul(mats[n][1], dense[n].t(), out=ys[n])
-            return torch.argmax(F.linear(head_x, dense["HEAD"]).float(), dim=1)
-
-        for _ in range(args.warmup):
-            dense_step()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.steps):
-            d_idx = dense_step()
-        b.record()
-        torch.cuda.synchronize()
-        d_ms = a.elapsed_time(b) / args.steps
-        d_bytes = sum(2 * dense[n].numel() + 2 * M_ROWS * dense[n].shape[1] + 2 * M_ROWS * dense[n].shape[0]
-                      for n in order) + 2 * dense["HEAD"].numel() + 2 * M_ROWS * HIDDEN
-        dense_ctx = {"what": "the block GEMMs and the head argmax on the bf16 source weights via torch.matmul "
-                             "and torch.argmax (no tree acceptance); context, not a baseline",
-                     "ms_per_step": round(d_ms, 4), "bytes_per_step": int(d_bytes),
-                     "GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
-                     "w12_step_speedup": round(d_ms / ms_per_step, 3),
-                     "head_argmax_agrees": float((d_idx == head_idx[0]).float().mean())}
-        del dense
+    if keep_dense:
+        dense_ctx = dense_context(args, torch, dev, mats, dense, head_x, head_dense, layers, ms_per_step,
+                                  head_idx[0])
+        del dense, head_dense
         torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(mats, synth, torch)
+        cpu = cpu_baseline(mats[0], synth, torch)
 
     line = {
         "metric": METRIC,
@@ -313,16 +291,21 @@ def main():
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "config": {
-            "workload": "verify pass of one 27B-class block (Wq|Wk|Wv 8192x5120, Wo 5120x6144, "
-                        "Wgate|Wup 34816x5120, Wdown 5120x17408) + 152064x5120 LM-head argmax "
-                        "+ 32-node tree acceptance, all weights W12",
-            "rows": M_ROWS,
+            "workload": f"verify pass of a {layers}-layer 27B-class stack (per layer Wq|Wk|Wv 8192x5120, "
+                        "Wo 5120x6144, Wgate|Wup 34816x5120, Wdown 5120x17408) + 152064x5120 LM-head "
+                        "argmax + 32-node tree acceptance, all weights W12, each layer its own weights "
+                        "and input rows",
+            "rows": M_ROWS, "layers": layers,
             "bytes_per_step": int(total_bytes),
             "graph": bool(args.graph),
         },
-        "breakdown_us": {n: round(v, 2) for n, v in kern_us.items()},
-        "block_gemm_GBps": round(block_gbps, 1),
-        "head_GBps": round(head_gbps, 1),
+        "us_per_pass": round(1000.0 * ms_per_step, 1),
+        "us_per_layer": round(block_us / layers, 2),
+        "block_gemm_GBps": round(block_bytes / (block_us * 1e-6) / 1e9, 1),
+        "head_GBps": round(gbps_of["HEAD"], 1),
+        "call_us": {n: round(v, 2) for n, v in call_us.items()},
+        "call_GBps": {n: round(v, 1) for n, v in gbps_of.items() if n != "TREE"},
+        "instrumented_ms_per_step": round(instrumented_ms, 4),
         "pack_GBps_bf16_in": round(pack_gbps, 1),
         "accepted": {"accept_len": int(acc[0]), "bonus": int(bonus[0])},
         "roofline": roofline,
@@ -330,6 +313,91 @@ def main():
         "dense_bf16_context": dense_ctx,
     }
     print(json.dumps(line), flush=True)
+
+
+def dense_context(args, torch, dev, mats, dense, head_x, head_dense, layers, ms_w12, idx_w12):
+    """Context only: the same pass on the dense bf16 source weights through
+    torch.matmul (hipBLASLt) and torch.argmax, timed the same way."""
+    F = torch.nn.functional
+    order = [name for name, _, _ in LAYER_SHAPES]
+    ys = {name: torch.empty(M_ROWS, n, dtype=torch.bfloat16, device=dev) for name, n, _ in LAYER_SHAPES}
+
+    def dense_step():
+        for li in range(layers):
+            for name in order:
+                torch.matmul(mats[li][name][1], dense[li][name].t(), out=ys[name])
+        return torch.argmax(F.linear(head_x, head_dense).float(), dim=1)
+
+    for _ in range(max(1, args.warmup)):
+        dense_step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        d_idx = dense_step()
+    b.record()
+    torch.cuda.synchronize()
+    d_ms = a.elapsed_time(b) / args.steps
+    d_bytes = sum(2 * dense[li][n].numel() + 2 * M_ROWS * dense[li][n].shape[1] + 2 * M_ROWS * dense[li][n].shape[0]
+                  for li in range(layers) for n in order) + 2 * head_dense.numel() + 2 * M_ROWS * HIDDEN
+    return {"what": "the pass's GEMMs and the head argmax on the bf16 source weights via torch.matmul "
+                    "and torch.argmax (no tree acceptance); context, not a baseline",
+            "ms_per_step": round(d_ms, 4), "bytes_per_step": int(d_bytes),
+            "GBps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+            "w12_step_speedup": round(d_ms / ms_w12, 3),
+            "head_argmax_agrees": float((d_idx == idx_w12).float().mean())}
+
+
+def run_block(args, w12, synth, torch, dev):
+    """One 27B-class block + the LM head + tree at M=32: the pass with one
+    layer (a quick line for development; the weights then fit in the
+    last-level cache between steps, so it flatters the block GEMMs)."""
+    args.layers = 1
+    return run_pass(args, w12, synth, torch, dev)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=LAYERS, help="layers of the pass workload (default 64)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense bf16 context timing of the same pass")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="size of the calibration copy launched after timing (0 = none)")
+    ap.add_argument("--workload", choices=("pass", "block", "batched", "sweep", "qpass", "tree"), default="pass",
+                    help="pass: 64 layers + LM head argmax + tree acceptance at M=32 (the headline line); "
+                         "block: the same with one layer; "
+                         "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
+                         "and 2%% outliers; "
+                         "sweep: Wgate|Wup 34816x5120 over M = 1 ... 512; "
+                         "qpass: one block + head through the Q pass (8-bit view only) next to the exact pass; "
+                         "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the verify path runs on one GPU here; across GPUs the weights would shard by "
+              "32-channel strips (column-parallel layers, the LM head) or 256-column records (row-parallel ones).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w12_weight_streaming_amd as w12
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w12.lib()
+    fn = {"pass": run_pass, "block": run_block, "batched": run_batched, "sweep": run_sweep,
+          "qpass": run_qpass, "tree": run_tree}[args.workload]
+    return fn(args, w12, synth, torch, dev)
 
 
 def clone_packed(w12, pw):
@@ -494,10 +562,11 @@ def run_qpass(args, w12, synth, torch, dev):
     """The block step at M=32 through the Q pass (QKV, O, UP, DOWN GEMMs and
     the LM-head argmax, reading only the 8-bit view of every record), next to
     the exact pass, with the head's top-1 agreement between the two."""
-    mats, _ = build_block(w12, synth, torch, dev)
+    layers, _, _ = pack_layers(w12, synth, torch, dev, 1)
+    mats = layers[0]
+    head_pw, head_x, _, _ = pack_head(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
     outs = {n: torch.empty(M_ROWS, mats[n][0].n, dtype=torch.bfloat16, device=dev) for n in order}
-    head_pw, head_x = mats["HEAD"]
     ws = w12.workspace(max(w12.gemm_workspace_bytes(mats[n][0].n, mats[n][0].k, M_ROWS)
                            for n in order + ["HEAD"]), dev)
 
@@ -541,81 +610,38 @@ def run_qpass(args, w12, synth, torch, dev):
     print(json.dumps(line), flush=True)
 
 
-def run_stack(args, w12, synth, torch, dev):
-    """64 blocks of the 27B-class shape in sequence at M=32 (about 33 GB of W12
-    records): every GEMM of a layer after the previous one, eager and as a
-    replayed graph."""
-    layers = 64
-    shapes = (("QKV", Q_OUT + 2 * KV_OUT, HIDDEN), ("O", HIDDEN, Q_OUT), ("UP", 2 * FFN, HIDDEN),
-              ("DOWN", HIDDEN, FFN))
-    mats = []
-    for li in range(layers):
-        row = []
-        for j, (name, n, k) in enumerate(shapes):
-            w = synth.weights_bf16(n, k, seed=1_000_000 * 3 + 1000 * li + j + 1, device=dev)
-            row.append(w12.w12_pack(w, check=li == 0))
-            del w
-        mats.append(row)
-        if li % 16 == 15:
-            log(f"packed {li + 1} layers")
-    xs = {k: synth.activations_bf16(M_ROWS, k, seed=1_000_000 * 3 + 500 + k, device=dev)
-          for k in {k for _, _, k in shapes}}
-    ys = {name: torch.empty(M_ROWS, n, dtype=torch.bfloat16, device=dev) for name, n, _ in shapes}
-    ws = w12.workspace(max(w12.gemm_workspace_bytes(n, k, M_ROWS) for _, n, k in shapes), dev)
-
-    def one_pass(_=0):
-        for row in mats:
-            for (name, n, k), pw in zip(shapes, row):
-                w12.w12_gemm(pw, xs[k], out=ys[name], ws=ws)
-
-    for _ in range(max(1, args.warmup)):
-        one_pass()
-    torch.cuda.synchronize()
-    reps = max(3, min(args.steps, 10))
-    eager_us = time_events(one_pass, reps)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        one_pass()
-    graph.replay()
-    torch.cuda.synchronize()
-    graph_us = time_events(lambda i: graph.replay(), reps)
-    nbytes = sum(gemm_bytes(pw, M_ROWS, 2) for row in mats for pw in row)
-    best = min(eager_us, graph_us)
-    gbps = nbytes / (best * 1e-6) / 1e9
-    line = {
-        "metric": "W12 verify pass of a 64-layer 27B-class stack at M=32: effective HBM GB/s",
-        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": max(1, args.warmup),
-        "ms_per_step": round(best / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "64 x (Wq|Wk|Wv 8192x5120, Wo 5120x6144, Wgate|Wup 34816x5120, "
-                               "Wdown 5120x17408), all W12, M=32, layers in order",
-                   "rows": M_ROWS, "bytes_per_pass": int(nbytes), "layers": layers},
-        "eager_ms_per_pass": round(eager_us / 1000.0, 4), "graph_ms_per_pass": round(graph_us / 1000.0, 4),
-        "us_per_layer": round(best / layers, 2), "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
-    }
-    print(json.dumps(line), flush=True)
-
-
-def cpu_baseline(mats, synth, torch):
-    """The oracle (decode + fp32 matmul) on a bounded sample: the Wo matrix
-    (5120 x 6144) at M=32, timed on this host's cores."""
+def cpu_baseline(layer, synth, torch):
+    """The oracle (decode + fp32 matmul) on a bounded sample of the pass:
+    the four GEMMs of one layer at M=32, timed on this host's cores, once
+    with every BLAS thread and once with one."""
     import numpy as np
 
-    from oracle import baseline, w12_format  # noqa: F401  (test infrastructure)
-    pw, x = mats["O"]
-    packed = {"records": pw.records.cpu().numpy(), "e_top": pw.e_top.cpu().numpy(),
-              "esc_off": pw.esc_off.cpu().numpy().view(np.uint32),
-              "esc": pw.esc.cpu().numpy()[:pw.n_esc].view(np.uint32)}
-    xb = synth.bits_u16(x)
-    first = baseline.time_cpu_verify_gemm(packed, pw.n, pw.k, xb, reps=1)
-    # about 10 s of CPU work in all: repeat the same GEMM
-    reps = max(1, min(60, int(10.0 / max(first["seconds"], 1e-3))))
-    r = baseline.time_cpu_verify_gemm(packed, pw.n, pw.k, xb, reps=reps)
-    nbytes = gemm_bytes(pw, M_ROWS, 4)
-    return {"value": round(nbytes / r["seconds"] / 1e9, 3), "unit": "GB/s",
-            "cores": r["threads"], "kind": "oracle",
-            "sample": f"Wo 5120x6144 W12 verify GEMM at M=32 (oracle decode + fp32 matmul), "
-                      f"{reps + 1} runs, {r['seconds'] * reps + first['seconds']:.1f} s of CPU time"}
+    from oracle import baseline  # test infrastructure: the timed CPU baseline
+    items = []
+    for name, _, _ in LAYER_SHAPES:
+        pw, x = layer[name]
+        packed = {"records": pw.records.cpu().numpy(), "e_top": pw.e_top.cpu().numpy(),
+                  "esc_off": pw.esc_off.cpu().numpy().view(np.uint32),
+                  "esc": pw.esc.cpu().numpy()[:pw.n_esc].view(np.uint32)}
+        items.append((packed, pw.n, pw.k, synth.bits_u16(x), gemm_bytes(pw, M_ROWS, 4)))
+    nbytes = sum(it[4] for it in items)
+
+    def leg(threads):
+        secs, used = 0.0, 0
+        for packed, n, k, xb, _ in items:
+            r = baseline.time_cpu_verify_gemm(packed, n, k, xb, reps=1, threads=threads)
+            secs += r["seconds"]
+            used = max(used, r["threads"])
+        return secs, used
+
+    s_all, t_all = leg(None)
+    s_one, t_one = leg(1)
+    return {"value": round(nbytes / s_all / 1e9, 3), "unit": "GB/s", "cores": t_all, "kind": "oracle",
+            "sample": f"one layer of the pass (QKV 8192x5120, O 5120x6144, UP 34816x5120, DOWN 5120x17408) "
+                      f"at M=32: oracle decode + fp32 matmul, {s_all:.1f} s with {t_all} BLAS threads "
+                      f"(the decode is single-threaded numpy)",
+            "one_thread": {"value": round(nbytes / s_one / 1e9, 3), "seconds": round(s_one, 2),
+                           "cores": t_one}}
 
 
 if __name__ == "__main__":

@@ -71,9 +71,16 @@ extern "C" {
 
 typedef enum {
   W12_OK = 0,
-  W12_EINVAL = -1, /* bad argument; nothing launched                     */
-  W12_ENOSPC = -2, /* workspace smaller than the matching query          */
-  W12_EHIP = -3    /* a HIP runtime call or kernel launch failed         */
+  W12_EINVAL = -1,  /* bad argument; nothing launched                    */
+  W12_ENOSPC = -2,  /* workspace smaller than the matching query         */
+  W12_EHIP = -3,    /* a HIP runtime call or kernel launch failed        */
+  W12_ECORRUPT = -4 /* the load-time check found weights that do not
+                       restore bit-for-bit: the weights are refused
+                       ([S1] 4.1, [S2]; [S3] "What is refused"). No call
+                       of the library returns it: w12_check reports a
+                       count through device memory, and the caller that
+                       reads a non-zero count refuses the weights with
+                       this status (the Python binding raises it).     */
 } w12_status;
 
 typedef enum { W12_Y_F32 = 0, W12_Y_BF16 = 1 } w12_ydtype;
@@ -97,7 +104,10 @@ int w12_abi_version(void);
 int64_t w12_num_blocks(int64_t n, int64_t k);
 
 /*
- * w12_pack_plan -- first half of packing ([S1] 4.1: conversion at load).
+ * w12_pack_plan -- first half of packing ([S1] 4.1: the weights are
+ * converted once, at load; per output channel the 16-binade exponent window
+ * holding the most weights, everything outside it on the escape list;
+ * [S2] W12 paragraph).
  *   w        [n, k] bf16 bit patterns, row-major (read only).
  *   e_top    [n] out: window tops E_n.
  *   esc_off  [w12_num_blocks(n,k) + 1] out: escape offsets; esc_off[last]
@@ -107,7 +117,9 @@ w12_status w12_pack_plan(const uint16_t *w, int64_t n, int64_t k,
                          uint8_t *e_top, uint32_t *esc_off, hipStream_t stream);
 
 /*
- * w12_pack -- second half: writes the records and the escape entries.
+ * w12_pack -- second half of packing ([S1] 4.1; [S2]): writes the 12 KB
+ * records (8-bit view plane, then low-nibble plane) and the escape entries
+ * (exact bf16 bits of every weight outside its channel's window).
  *   e_top, esc_off  from w12_pack_plan on the same w.
  *   records         [n*k*3/2] out.
  *   esc             [esc_capacity] out; entries past esc_capacity are
@@ -126,11 +138,24 @@ w12_status w12_decode(const w12_matrix *w, uint16_t *out, hipStream_t stream);
 
 /* w12_check -- load-time bit-for-bit check ([S1] 4.1, [S2]): decodes every
  * weight and ADDS the number that differ from ref [n, k] to *mismatches
- * (device u64; the caller zeroes it). Non-zero means refuse the weights. */
+ * (device u64; the caller zeroes it). Non-zero means refuse the weights
+ * (W12_ECORRUPT). An escape block whose offsets are inconsistent
+ * (esc_off[b+1] < esc_off[b], esc_off[b+1] > esc_off[last], or more than
+ * the block's 1024 weights) counts all of its 1024 weights as mismatches and
+ * reads no entry. Reads of esc stay below esc_off[last], which the caller
+ * vouches for as the length of esc. w12_decode applies the same bounds; its
+ * output for such a block is the records' codes without escapes. */
 w12_status w12_check(const w12_matrix *w, const uint16_t *ref,
                      unsigned long long *mismatches, hipStream_t stream);
 
-/* Workspace bytes w12_gemm needs for this shape (host output). */
+/* Workspace bytes w12_gemm needs for this shape (host output). The
+ * workspace holds what the deterministic split of the k reduction needs
+ * ([S1] 4.1: stream-K with a fixed summation order): one arrival counter per
+ * output tile, the partial sums of the tiles split between workgroups, the
+ * argmax keys of the head, and x rearranged into matrix-core fragments. The
+ * size depends on the device's compute-unit count, which the library reads
+ * once per device id and keeps for the life of the process (the only state
+ * the library holds besides the no-allocation entry point's scratch). */
 w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
 
 /*
@@ -230,6 +255,9 @@ w12_status w12_tree_build(int32_t num_req, int32_t positions, int32_t k, const f
  * A tree with no nodes, a root parent other than -1, a parent outside
  * [0, i), or offsets outside [0, total_nodes] gets accept_len = bonus = -1
  * and an all -1 path (device-detected; the call itself returns W12_OK).
+ * total_nodes (the length of parent, token, argmax and path) is what the
+ * kernel checks device-side offsets against, so that a corrupt node_off
+ * never reads or writes past those arrays.
  */
 w12_status tree_accept(int32_t num_trees, const int32_t *node_off,
                        int32_t total_nodes, const int32_t *parent,

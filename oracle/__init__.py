@@ -24,11 +24,15 @@ Sources (the pages these functions follow):
 Modules:
   w12_format -- pack / decode / layout / sizes           (parity pinned)
   verify     -- FP64 GEMM reference + bound, head argmax with near-tie
-                classification, brute-force tree acceptance (parity pinned)
-  baseline   -- the timed CPU baseline (oracle decode + FP32 matmul)
+                classification, the top-k candidate ids of a row (which the
+                tests draw mismatching draft tokens from), brute-force tree
+                acceptance (parity pinned)
+  tree_build -- best-first draft trees under a shared row budget (pinned)
+  baseline   -- the timed CPU baseline (oracle decode + FP32 matmul), pinned
+                to the fp64 GEMM reference within the GEMM bound
 
 Every function here is pinned by a `-m "not gpu"` test against something
-other than itself (closed forms, IEEE value semantics, brute force, the
-pages' worked example); none is "parity unpinned".
+other than itself (closed forms, IEEE value semantics, brute force over
+exact integer data, the pages' worked example); none is "parity unpinned".
 """
 from . import w12_format, verify, baseline  # noqa: F401

@@ -7,7 +7,6 @@ leg is its one caller outside tests.
 """
 from __future__ import annotations
 
-import os
 import time
 
 import numpy as np
@@ -22,17 +21,33 @@ def cpu_verify_gemm(packed: dict, n: int, k: int, x_bits: np.ndarray) -> np.ndar
     return xf @ wf.T
 
 
+def blas_threads() -> int:
+    """Threads numpy's BLAS runs its matmul with (read from the loaded BLAS
+    library itself); the decode is plain numpy, one thread."""
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            return int(max(d["num_threads"] for d in info))
+    except Exception:  # threadpoolctl missing or unreadable: say so with 0
+        pass
+    return 0
+
+
 def time_cpu_verify_gemm(packed: dict, n: int, k: int, x_bits: np.ndarray,
-                         reps: int = 1) -> dict:
+                         reps: int = 1, threads: int | None = None) -> dict:
     """Wall time of `reps` CPU verify GEMMs; returns seconds per GEMM and the
-    thread count numpy's BLAS was allowed (from the usual env variables)."""
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        cpu_verify_gemm(packed, n, k, x_bits)
-    dt = (time.perf_counter() - t0) / reps
-    threads = None
-    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
-        if os.environ.get(var):
-            threads = int(os.environ[var])
-            break
-    return {"seconds": dt, "threads": threads or os.cpu_count()}
+    BLAS thread count used. `threads` limits the BLAS pool for this call
+    (None: as loaded)."""
+    def run():
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            cpu_verify_gemm(packed, n, k, x_bits)
+        return (time.perf_counter() - t0) / reps
+
+    if threads is None:
+        np.ones((2, 2), np.float32) @ np.ones((2, 2), np.float32)  # load BLAS before asking
+        return {"seconds": run(), "threads": blas_threads()}
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        return {"seconds": run(), "threads": blas_threads()}

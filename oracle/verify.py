@@ -94,8 +94,11 @@ def head_argmax(x_bits: np.ndarray, w_bits: np.ndarray, chunk: int = 8192):
 
 
 def head_topk(x_bits: np.ndarray, w_bits: np.ndarray, topk: int = 16, chunk: int = 8192):
-    """Ids of the top-k fp64 logits per row (any order among them); used only
-    to draw synthetic draft tokens from a row's strongest candidates."""
+    """The k strongest vocabulary ids of each row: the first k ids in the
+    order (fp64 logit descending, id ascending), so ties at the cut keep the
+    lowest ids; returned in that order. The tests draw the mismatching draft
+    tokens of synthetic trees from these ([S1] 4.2: a 32-node tree branches
+    over each position's top-16 candidates)."""
     x = bf16_to_f64(x_bits)
     m = x.shape[0]
     cur_val = np.full((m, 0), -np.inf)

@@ -42,6 +42,7 @@ def test_every_declared_symbol_is_exported(L):
     assert set(declared_functions()) <= set(w.exported_symbols())
     assert L.w12_abi_version() == 1
     assert b"EINVAL" in L.w12_strerror(-1)
+    assert b"ECORRUPT" in L.w12_strerror(-4) and w.W12_ECORRUPT == -4
 
 
 def test_num_blocks_and_shape_rules(L):

@@ -128,13 +128,30 @@ def test_check_detects_corruption(w12):
     pw.records.copy_(rec)
     pw.e_top[3] += 1
     assert w12.w12_check(pw, t) >= 1
+    with pytest.raises(w12.W12Error) as e:
+        w12.w12_require_exact(pw, t)
+    assert e.value.status == w12.W12_ECORRUPT
     pw.e_top[3] -= 1
+    assert w12.w12_check(pw, t) == 0
+    w12.w12_require_exact(pw, t)
+    # corrupt escape offsets (the last one, the escape count, stays): a block
+    # whose offsets jump past the count or run backwards is counted as 1024
+    # mismatches, and no entry is read outside the list
+    off = pw.esc_off.clone()
+    nb = pw.esc_off.numel() - 1
+    pw.esc_off[5] = 0x7FFFFFF0                      # blocks 4 and 5 inconsistent
+    assert w12.w12_check(pw, t) >= 2 * 1024
+    pw.esc_off.copy_(off)
+    pw.esc_off[nb // 2] = 0                         # offsets decrease into it
+    assert w12.w12_check(pw, t) >= 1
+    pw.esc_off.copy_(off)
     assert w12.w12_check(pw, t) == 0
 
 
 # ----------------------------------------------------------------------------- GEMM
 
-GEMM_SHAPES = [(1024, 1024), (96, 768), (320, 1792)]
+# (640, 256): one record per strip, so every unit ends a tile
+GEMM_SHAPES = [(1024, 1024), (96, 768), (320, 1792), (640, 256)]
 ROWS = [1, 2, 3, 5, 8, 9, 12, 13, 15, 16, 17, 32, 33, 64, 100, 192, 256, 384, 512]
 
 
@@ -451,29 +468,59 @@ def test_full_size_block_matrices(w12, name, n, k):
         assert V.within_tolerance(y[:, cols], y_ref, bound).all(), (name, m)
 
 
-def test_full_size_batched_m192(w12):
-    n, k = 5120, 17408
-    w = gen(n, k, 77, p_zero=0.03, p_outlier=0.02, device=DEV)
+@pytest.mark.parametrize("name,n,k,seed", [("Wdown", 5120, 17408, 77), ("Wup", 17408, 5120, 79)])
+def test_full_size_batched_m192(w12, name, n, k, seed):
+    """The batched verify shapes at 192 rows with 3% zeros and 2% x64
+    outliers (~3.2% escapes), on sampled columns."""
+    say("batched m=192", name, n, k)
+    w = gen(n, k, seed, p_zero=0.03, p_outlier=0.02, device=DEV)
     pw = w12.w12_pack(w)
-    x = synth.activations_bf16(192, k, 78, device=DEV)
+    assert pw.n_esc > 0.03 * n * k
+    x = synth.activations_bf16(192, k, seed + 1, device=DEV)
     y = host(w12.w12_gemm(pw, x))
-    rng = np.random.default_rng(3)
-    cols = rng.choice(n, 48, replace=False)
+    rng = np.random.default_rng(seed)
+    cols = np.concatenate([rng.choice(n - 32, 48, replace=False), np.arange(n - 32, n)])
     y_ref, bound = V.gemm_ref(synth.bits_u16(x), synth.bits_u16(w[torch.as_tensor(cols, device=DEV)]))
     assert V.within_tolerance(y[:, cols], y_ref, bound).all()
 
 
-def test_full_size_head_argmax(w12):
+@pytest.mark.timeout(400)
+def test_full_size_head_argmax_and_config4_tree(w12):
+    """LM head 152064x5120 at 32 rows: every row's fused argmax against the
+    oracle (exact away from near-ties), then a 32-node tree whose
+    mismatching tokens come from the parent row's oracle top-16 candidates
+    ([S1] 4.2), accepted on the GPU's argmax and compared with the oracle's
+    acceptance on the same argmax and, when no row is a near-tie, on the
+    oracle's own argmax."""
     n, k, m = 152064, 5120, 32
     w = gen(n, k, 4242, device=DEV)
     pw = w12.w12_pack(w)
     x = synth.activations_bf16(m, k, 4243, device=DEV)
     idx, _ = w12.w12_head_argmax(pw, x)
-    rows = [0, 7, 31]
+    idx = host(idx)
     wb = synth.bits_u16(w)
     del w
-    ref_idx, _, cands = V.head_argmax(synth.bits_u16(x)[rows], wb, chunk=16384)
-    check_argmax(host(idx)[rows], ref_idx, cands)
+    xb = synth.bits_u16(x)
+    say("full head: oracle argmax over 32 rows")
+    ref_idx, _, cands = V.head_argmax(xb, wb, chunk=16384)
+    near = check_argmax(idx, ref_idx, cands)
+    say("full head: near-tie rows", near, "; oracle top-16")
+    top16 = V.head_topk(xb, wb, topk=16, chunk=16384)
+    assert np.array_equal(top16[:, 0], ref_idx)
+    for seed in range(4):
+        parent, token = synth.random_tree(m, 16, idx, top16, 0.7, seed=4_000_000 + seed, vocab=n)
+        drawn = [token[i] for i in range(1, m) if token[i] != idx[parent[i]]]
+        assert all(t in set(top16[parent[i]].tolist()) for i, t in
+                   ((i, token[i]) for i in range(1, m)) if t != idx[parent[i]])
+        got = run_tree(w12, [0, m], parent, token, idx)
+        ref = V.tree_accept([0, m], parent, token, idx)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r)
+        if near == 0:
+            ref2 = V.tree_accept([0, m], parent, token, ref_idx)
+            for g, r in zip(got, ref2):
+                assert np.array_equal(g, r)
+        say("config-4 tree", seed, "accept_len", got[0][0], "mismatching drafts", len(drawn))
 
 
 def test_full_size_head_shape_four_strip_tiles(w12):

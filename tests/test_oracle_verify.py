@@ -186,3 +186,76 @@ def test_multiple_trees_and_invalid():
     assert acc[3] == -1
     # tree 4: empty -> invalid
     assert acc[4] == -1 and bonus[4] == -1
+
+
+# --------------------------------------------------------------------------- top-k candidates
+
+@pytest.mark.parametrize("chunk", [3, 16, 50, 8192])
+def test_head_topk_against_brute_force_with_ties(chunk):
+    """The k strongest ids of a row: brute force over exact integer logits,
+    ordered by (logit descending, id ascending), so ties at the cut keep the
+    lowest ids. Integer data makes every logit exact and ties common; chunks
+    smaller than k and not dividing the vocabulary cross the merge path."""
+    rng = np.random.default_rng(11)
+    xi = rng.integers(-2, 3, (5, 40))
+    wi = rng.integers(-2, 3, (203, 40))
+    xb, wb = bits_of(xi.astype(np.float32)), bits_of(wi.astype(np.float32))
+    for topk in (1, 4, 16):
+        got = V.head_topk(xb, wb, topk=topk, chunk=chunk)
+        assert got.shape == (5, topk)
+        for r in range(5):
+            L = [int(sum(int(a) * int(b) for a, b in zip(xi[r], wi[v]))) for v in range(203)]
+            want = sorted(range(203), key=lambda v: (-L[v], v))[:topk]
+            assert set(got[r].tolist()) == set(want)
+            assert len(set(got[r].tolist())) == topk
+
+
+def test_head_topk_first_is_the_argmax_and_real_valued_rows():
+    """On real-valued data the top-1 is the head argmax, and every returned
+    logit is >= every logit left out (checked on fp64 logits formed one
+    product at a time)."""
+    rng = np.random.default_rng(12)
+    x = bits_of(rng.standard_normal((3, 64)).astype(np.float32))
+    w = bits_of((rng.standard_normal((300, 64)) * 0.05).astype(np.float32))
+    top = V.head_topk(x, w, topk=16, chunk=37)
+    idx, _, _ = V.head_argmax(x, w, chunk=37)
+    xf, wf = V.bf16_to_f64(x), V.bf16_to_f64(w)
+    for r in range(3):
+        L = np.array([sum(float(a) * float(b) for a, b in zip(xf[r], wf[v])) for v in range(300)])
+        kept = set(top[r].tolist())
+        assert idx[r] in kept
+        assert min(L[list(kept)]) >= max(L[[v for v in range(300) if v not in kept]])
+
+
+# --------------------------------------------------------------------------- timed CPU baseline
+
+def test_cpu_baseline_gemm_within_tolerance_of_the_reference():
+    """The timed baseline (oracle decode + fp32 matmul) must give the GEMM the
+    pages define, within the same bound the GPU is held to."""
+    import synth
+    from oracle import baseline, w12_format as F
+    n, k, m = 96, 768, 5
+    bits = synth.bits_u16(synth.weights_bf16(n, k, 901, p_zero=0.05, p_outlier=0.02))
+    xb = synth.bits_u16(synth.activations_bf16(m, k, 902))
+    y = baseline.cpu_verify_gemm(F.pack(bits), n, k, xb)
+    y_ref, bound = V.gemm_ref(xb, bits)
+    assert y.dtype == np.float32 and y.shape == (m, n)
+    assert V.within_tolerance(y, y_ref, bound).all()
+    # the decoded weights are the source: one-hot rows pick exact columns
+    eye = np.zeros((4, k), np.uint16)
+    eye[np.arange(4), [0, 255, 256, 767]] = 0x3F80
+    y1 = baseline.cpu_verify_gemm(F.pack(bits), n, k, eye)
+    wf = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(y1, wf[:, [0, 255, 256, 767]].T)
+
+
+def test_cpu_baseline_reports_the_threads_it_ran_with():
+    import synth
+    from oracle import baseline, w12_format as F
+    n, k = 64, 512
+    bits = synth.bits_u16(synth.weights_bf16(n, k, 903))
+    xb = synth.bits_u16(synth.activations_bf16(4, k, 904))
+    one = baseline.time_cpu_verify_gemm(F.pack(bits), n, k, xb, threads=1)
+    assert one["threads"] == 1 and one["seconds"] > 0
+    allc = baseline.time_cpu_verify_gemm(F.pack(bits), n, k, xb)
+    assert allc["threads"] >= 1

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw12.so")
 
-W12_OK, W12_EINVAL, W12_ENOSPC, W12_EHIP = 0, -1, -2, -3
+W12_OK, W12_EINVAL, W12_ENOSPC, W12_EHIP, W12_ECORRUPT = 0, -1, -2, -3, -4
 W12_Y_F32, W12_Y_BF16 = 0, 1
 MFMA_MIN_ROWS = 16
 MAX_ROWS = 512
@@ -176,8 +176,16 @@ def w12_pack(w: torch.Tensor, check: bool = True) -> PackedW12:
     if check:
         bad = w12_check(pw, w)
         if bad:
-            raise RuntimeError(f"W12 load-time check failed: {bad} weights differ")
+            raise W12Error(W12_ECORRUPT, f"w12_pack load-time check: {bad} weights differ")
     return pw
+
+
+def w12_require_exact(pw: PackedW12, ref: torch.Tensor) -> None:
+    """The load-time refusal: raise W12Error(W12_ECORRUPT) unless every
+    weight of pw restores bit-for-bit to ref."""
+    bad = w12_check(pw, ref)
+    if bad:
+        raise W12Error(W12_ECORRUPT, f"w12_check: {bad} weights differ")
 
 
 def w12_decode(pw: PackedW12) -> torch.Tensor:

@@ -134,6 +134,7 @@ const char* w12_strerror(int status) {
     case W12_EINVAL: return "W12_EINVAL: invalid argument";
     case W12_ENOSPC: return "W12_ENOSPC: workspace too small";
     case W12_EHIP: return "W12_EHIP: HIP runtime or launch error";
+    case W12_ECORRUPT: return "W12_ECORRUPT: weights do not restore bit-for-bit (refused)";
     default: return "W12: unknown status";
   }
 }
@@ -190,6 +191,7 @@ w12_status w12_gemm_qpass(const w12_matrix* w, const uint16_t* x, int64_t m, voi
                           void* ws, size_t ws_bytes, hipStream_t stream) {
   return gemm_entry(w, x, m, y, ytype, ws, ws_bytes, stream, true);
 }
+
 
 w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
   return w12_gemm_workspace(n, k, m, bytes);

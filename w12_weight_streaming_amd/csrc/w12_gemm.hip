@@ -411,7 +411,10 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
   int any = 0;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    cq[q] = max(__builtin_amdgcn_readfirstlane((int)(s.off[q].y - s.off[q].x)), 0);
+    // a block holds at most 1024 weights: corrupt offsets cannot make the
+    // patch loop run longer (entries are read through a resource that ends
+    // at the escape count, so reads stay in bounds either way)
+    cq[q] = min(max(__builtin_amdgcn_readfirstlane((int)(s.off[q].y - s.off[q].x)), 0), 1024);
     any |= cq[q];
   }
 #pragma unroll
@@ -1163,8 +1166,10 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
+  // escape entries read through a resource that ends at the escape count
+  const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
   const Big8Loads<QP> L{a, u0, u1, sw, kg, RK, S, (uint32_t)RK * kRecBytes, (uint32_t)(lane * 16),
-                    (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, 0xFFFFFFFFu)};
+                    (uint32_t)(kHiBytes + lane * 8), make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu)};
   const uint32_t plo = patch_lane_off(lane);
 
   // x staging: thread piece j = tid & 7 (16 B) of row 64 i + (tid >> 3)
@@ -1271,7 +1276,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   auto step = [&](const Big8Slot& sl, int buf) __attribute__((always_inline)) {
     const int sq = 4 * cur.p + sw;
     if (cur.h == 0 && (cur.r == 0 || cur.u == u0)) bias = strip_bias2(a.w.e_top, sq, sq < S, lane);
-    const int cnt = __builtin_amdgcn_readfirstlane((int)(sl.off[1] - sl.off[0]));
+    const int cnt = min(__builtin_amdgcn_readfirstlane((int)(sl.off[1] - sl.off[0])), 1024);
     const char* xb = lds + buf * Lds::kX + x_r;
     bf16x8 bq[MT];
 #pragma unroll

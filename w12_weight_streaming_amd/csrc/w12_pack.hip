@@ -227,8 +227,12 @@ __global__ __launch_bounds__(256) void decode_kernel(MatrixArgs a, uint16_t* __r
   const uint2 lo = *reinterpret_cast<const uint2*>(a.rec + rb + kHiBytes + q.t * 512 + lane * 8);
   uint32_t p[8];
   decode16(hi, lo, bias2_of(a.e_top[q.n]), p);
-  const uint32_t o = a.esc_off[b];
-  const uint32_t cnt = a.esc_off[b + 1] - o;
+  // A block's offsets must increase, stay within the escape count and hold
+  // at most the block's 1024 weights; otherwise no entry is read and, in
+  // the check, every weight of the block counts as a mismatch.
+  const uint32_t o = a.esc_off[b], o1 = a.esc_off[b + 1], n_esc = a.esc_off[a.nb];
+  const bool sane = o <= o1 && o1 <= n_esc && o1 - o <= 1024u;
+  const uint32_t cnt = sane ? o1 - o : 0u;
   if (cnt) {
     uint32_t* wb = buf[wave];
     *reinterpret_cast<uint4*>(wb + lane * 8) = make_uint4(p[0], p[1], p[2], p[3]);
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(256) void decode_kernel(MatrixArgs a, uint16_t* __r
       const uint32_t d = p[i] ^ rr[i];
       bad += ((d & 0xFFFFu) != 0) + ((d >> 16) != 0);
     }
-    bad = wave_sum_u32(bad);
+    bad = sane ? wave_sum_u32(bad) : 1024u;
     if (lane == 0 && bad) atomicAdd(mism, (unsigned long long)bad);
   }
 }
