@@ -174,6 +174,29 @@ w12_status w12_gemm(const w12_matrix *w, const uint16_t *x, int64_t m,
                     void *y, int ytype, void *ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/*
+ * w12_gemm_noalloc -- w12_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, bit for bit, with the
+ * workspace taken from a static device array of the library
+ * (W12_NOALLOC_SCRATCH_BYTES per device, reserved when the library is
+ * loaded and held until the process ends). The call allocates nothing.
+ *   Arguments and layouts as w12_gemm, without ws / ws_bytes.
+ *   Returns W12_ENOSPC, before launching anything, when w12_gemm_workspace
+ *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES (at 256 compute units:
+ *   every m <= 512 fits for k <= 400000; at 16 <= m <= 64 the x fragments
+ *   need 128 * k bytes).
+ *   The first call on a device looks up the array's device address and
+ *   enqueues one kernel on `stream` that zero-fills it; every completed call
+ *   leaves its counters at zero again.
+ *   All calls on one device share that device's array: calls that overlap in
+ *   time on one device (other streams, other threads) race and give wrong
+ *   results. Serialise them.
+ */
+#define W12_NOALLOC_SCRATCH_BYTES (64u << 20)
+w12_status w12_gemm_noalloc(const w12_matrix *w, const uint16_t *x, int64_t m,
+                            void *y, int ytype, hipStream_t stream);
+
 /* Workspace bytes w12_head_argmax needs (host output). */
 w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
 

@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "w12_head_argmax_workspace": (ctypes.c_int, [i64, i64, i64, ctypes.POINTER(sz)]),
             "w12_head_argmax": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "w12_gemm_qpass": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
+            "w12_gemm_noalloc": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp]),
             "w12_head_argmax_qpass": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "tree_accept": (ctypes.c_int, [i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "w12_tree_build_workspace": (ctypes.c_int, [i32, i32, ctypes.POINTER(sz)]),
@@ -81,7 +82,8 @@ def exported_symbols():
     return ["w12_strerror", "w12_abi_version", "w12_num_blocks", "w12_pack_plan", "w12_pack",
             "w12_decode", "w12_check", "w12_gemm_workspace", "w12_gemm",
             "w12_head_argmax_workspace", "w12_head_argmax", "w12_gemm_qpass",
-            "w12_head_argmax_qpass", "tree_accept", "w12_tree_build_workspace", "w12_tree_build"]
+            "w12_head_argmax_qpass", "tree_accept", "w12_tree_build_workspace", "w12_tree_build",
+            "w12_gemm_noalloc"]
 
 
 def _ok(status: int, what: str):
@@ -233,6 +235,27 @@ def w12_gemm(pw: PackedW12, x: torch.Tensor, out: torch.Tensor | None = None,
     d = pw.desc()
     fn, name = (lib().w12_gemm_qpass, "w12_gemm_qpass") if qpass else (lib().w12_gemm, "w12_gemm")
     _ok(fn(ctypes.byref(d), _ptr(x), m, _ptr(out), yt, _ptr(ws), ws.numel(), _stream(x.device)), name)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w12_gemm_noalloc(pw: PackedW12, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """w12_gemm with the library's own static scratch as workspace: no
+    device allocation in the call (out is the caller's). Calls that overlap
+    on one device race."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if k != pw.k:
+        raise ValueError(f"x has k={k}, matrix has k={pw.k}")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, pw.n):
+        raise ValueError("out must be [m, n] float32 or bfloat16")
+    _need(out, out.dtype, "out", 2)
+    yt = W12_Y_F32 if out.dtype == torch.float32 else W12_Y_BF16
+    d = pw.desc()
+    _ok(lib().w12_gemm_noalloc(ctypes.byref(d), _ptr(x), m, _ptr(out), yt, _stream(x.device)),
+        "w12_gemm_noalloc")
     return out
 
 

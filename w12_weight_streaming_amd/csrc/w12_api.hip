@@ -192,6 +192,81 @@ w12_status w12_gemm_qpass(const w12_matrix* w, const uint16_t* x, int64_t m, voi
   return gemm_entry(w, x, m, y, ytype, ws, ws_bytes, stream, true);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------- no-allocation GEMM
+//
+// w12_gemm_noalloc runs w12_gemm's kernels with their workspace in `scratch`,
+// a file-scope device array: one copy per device, held until the process
+// ends. In host code the array's name is not a device address; the address
+// each device gives for it is looked up once per device, with that device
+// current, and only that pointer is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[W12_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Zero-fill of the scratch array at set-up: the workspace's arrival counters
+// and argmax keys must start at zero (every completed call leaves them at
+// zero again). A kernel rather than hipMemsetAsync, so that a set-up that
+// happens inside stream capture records a kernel node.
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+  std::atomic<int> state{0};  // 0 not set up, 1 setting up, 2 ready, 3 failed
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The scratch array's device address on the current device (nullptr on
+// failure). The first caller on a device looks it up and enqueues the clear
+// on its stream; callers racing with it wait until it is done.
+void* scratch_ptr(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  int st_ = slot.state.load(std::memory_order_acquire);
+  if (st_ == 2) return slot.ptr;
+  if (st_ == 3) return nullptr;
+  int expect = 0;
+  if (slot.state.compare_exchange_strong(expect, 1, std::memory_order_acq_rel)) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p) {
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p),
+                         (size_t)W12_NOALLOC_SCRATCH_BYTES / 16);
+      e = hipGetLastError();
+    }
+    slot.ptr = (e == hipSuccess) ? p : nullptr;
+    slot.state.store(e == hipSuccess && p ? 2 : 3, std::memory_order_release);
+    return slot.ptr;
+  }
+  while ((st_ = slot.state.load(std::memory_order_acquire)) == 1) {
+  }
+  return st_ == 2 ? slot.ptr : nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+w12_status w12_gemm_noalloc(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
+                            hipStream_t stream) {
+  if (!matrix_ok(w) || !x || !y || m < 1 || m > kMaxRows) return W12_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return W12_EINVAL;
+  if (ytype != W12_Y_F32 && ytype != W12_Y_BF16) return W12_EINVAL;
+  const int cu = num_cu();
+  if (cu <= 0) return W12_EHIP;
+  if (gemm_ws_bytes(w->n, w->k, m, cu) > (size_t)W12_NOALLOC_SCRATCH_BYTES) return W12_ENOSPC;
+  void* ws = scratch_ptr(stream);
+  if (!ws) return W12_EHIP;
+  return run_gemm(w, x, m, y, ytype, nullptr, nullptr, ws, W12_NOALLOC_SCRATCH_BYTES, stream,
+                  w12::kEpiY, false);
+}
 
 w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
   return w12_gemm_workspace(n, k, m, bytes);
