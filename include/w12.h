@@ -183,9 +183,10 @@ w12_status w12_gemm(const w12_matrix *w, const uint16_t *x, int64_t m,
  * loaded and held until the process ends). The call allocates nothing.
  *   Arguments and layouts as w12_gemm, without ws / ws_bytes.
  *   Returns W12_ENOSPC, before launching anything, when w12_gemm_workspace
- *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES (at 256 compute units:
- *   every m <= 512 fits for k <= 400000; at 16 <= m <= 64 the x fragments
- *   need 128 * k bytes).
+ *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES. No workspace part grows
+ *   with n or k, so at 256 compute units every accepted shape fits (the
+ *   largest workspace, 192-row launches, is 51.6 MB); a device with more
+ *   than about 330 compute units could exceed it at m > 64.
  *   The first call on a device looks up the array's device address and
  *   enqueues one kernel on `stream` that zero-fills it; every completed call
  *   leaves its counters at zero again.

@@ -67,12 +67,13 @@ def test_noalloc_equals_gemm_on_two_calls(w12, n, k, m1, m2):
             assert V.within_tolerance(got.cpu().numpy(), y_ref, bound).all()
 
 
-def test_noalloc_rejects_a_shape_beyond_the_scratch(w12):
-    """16 <= m <= 64 needs 128 k bytes of x fragments: k = 2^20 does not fit
-    in 64 MiB; the call refuses before launching anything."""
-    n, k = 32, 1 << 20
-    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: the size check comes first
-    d = w12.W12Matrix(n, k, fake.value, fake.value, fake.value, fake.value)
-    st = w12.lib().w12_gemm_noalloc(ctypes.byref(d), fake, 64, fake, 0, ctypes.c_void_p(0))
-    assert st == w12.W12_ENOSPC
-    assert w12.NOALLOC_SCRATCH_BYTES == 64 << 20
+def test_noalloc_scratch_holds_every_workspace(w12):
+    """The scratch array holds the workspace of every shape the library
+    accepts on this device (rows up to 512 run as launches of at most 192,
+    and no workspace part grows with k), so no call is refused for size.
+    Only the size queries run here: nothing is launched."""
+    worst = 0
+    for n, k in ((32, 256), (152064, 5120), (5120, 17408), (2048, 1 << 20), (1 << 21, 1024)):
+        for m in (1, 16, 32, 33, 64, 65, 192, 193, 512):
+            worst = max(worst, w12.gemm_workspace_bytes(n, k, m))
+    assert 0 < worst <= w12.NOALLOC_SCRATCH_BYTES, worst
