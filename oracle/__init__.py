@@ -28,6 +28,9 @@ Modules:
                 tests draw mismatching draft tokens from), brute-force tree
                 acceptance (parity pinned)
   tree_build -- best-first draft trees under a shared row budget (pinned)
+  certified_head -- the certified INT8 LM head: INT8 copy with power-of-two
+                block scales, per-row Cauchy-Schwarz bounds, pruning and
+                exact rescoring (pinned)
   baseline   -- the timed CPU baseline (oracle decode + FP32 matmul), pinned
                 to the fp64 GEMM reference within the GEMM bound
 
@@ -35,4 +38,4 @@ Every function here is pinned by a `-m "not gpu"` test against something
 other than itself (closed forms, IEEE value semantics, brute force over
 exact integer data, the pages' worked example); none is "parity unpinned".
 """
-from . import w12_format, verify, baseline  # noqa: F401
+from . import w12_format, verify, baseline, certified_head  # noqa: F401
