@@ -312,6 +312,57 @@ def run_pass(args, w12, synth, torch, dev):
     print(json.dumps(line), flush=True)
 
 
+def run_cert(args, w12, synth, torch, dev):
+    """The certified INT8 head next to the W12 head: 152064x5120 at M=32,
+    both timed on the launch stream with events over back-to-back calls."""
+    import numpy as np
+
+    w = synth.weights_bf16(VOCAB, HIDDEN, seed=1_000_000 * 4 + 8, device=dev)
+    pw = w12.w12_pack(w, check=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    cert = w12.w12_cert8_pack(w, pw)
+    torch.cuda.synchronize()
+    cert_pack_s = time.perf_counter() - t0
+    del w
+    x = synth.activations_bf16(M_ROWS, HIDDEN, seed=1_000_000 * 4 + 508, device=dev)
+    ws = w12.workspace(64 << 20, dev, "bench")
+    wsc = w12.workspace(256 << 20, dev, "bench-cert")
+    head = lambda i: w12.w12_head_argmax(pw, x, ws=ws, with_max=False)
+    certified = lambda i: w12.w12_head_argmax_certified(pw, cert, x, ws=wsc, with_max=False)
+    for _ in range(args.warmup):
+        head(0)
+        certified(0)
+    torch.cuda.synchronize()
+    reps = max(10, args.steps)
+    t_head = min(time_events(head, reps) for _ in range(3))
+    t_cert = min(time_events(certified, reps) for _ in range(3))
+    idx_w, _ = w12.w12_head_argmax(pw, x, ws=ws, with_max=False)
+    idx_c, _, cnt = w12.w12_head_argmax_certified(pw, cert, x, ws=wsc, with_max=False)
+    cnt = cnt.cpu().numpy()
+    head_b = head_bytes(pw, M_ROWS)
+    # the INT8 pass reads the copy, W12's escape lists and x; the rescoring
+    # reads about 7.5 KB of records per rescored row
+    pass_b = cert.nbytes() + 4 * (pw.esc_off.numel() + pw.n_esc) + 2 * M_ROWS * HIDDEN
+    line = {
+        "metric": "LM-head argmax time at M=32 (152064x5120): certified INT8 head vs W12 head",
+        "value": round(t_cert, 2), "unit": "us", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(t_cert / 1000.0, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LM head 152064x5120 + argmax at M=32: INT8 copy pass (32-weight power-of-two "
+                               "block scales, W12 escapes exact), per-row Cauchy-Schwarz pruning, exact W12 "
+                               "rescoring of the survivors", "rows": M_ROWS},
+        "w12_head_us": round(t_head, 2),
+        "speedup_vs_w12_head": round(t_head / t_cert, 3),
+        "argmax_agrees_with_w12_head": float((idx_w == idx_c).float().mean()),
+        "rescored_per_row": {"median": int(np.median(cnt)), "max": int(cnt.max()), "of": VOCAB},
+        "bytes": {"w12_head": int(head_b), "int8_pass": int(pass_b), "int8_copy": int(cert.nbytes())},
+        "int8_pass_GBps": round(pass_b / (t_cert * 1e-6) / 1e9, 1),
+        "cert_pack_s": round(cert_pack_s, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def dense_context(args, torch, dev, mats, dense, head_x, head_dense, layers, ms_w12, idx_w12):
     """Context only: the same pass on the dense bf16 source weights through
     torch.matmul (hipBLASLt) and torch.argmax, timed the same way."""
@@ -365,14 +416,16 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the calibration copy launched after timing (0 = none)")
-    ap.add_argument("--workload", choices=("pass", "block", "batched", "sweep", "qpass", "tree"), default="pass",
+    ap.add_argument("--workload", choices=("pass", "block", "batched", "sweep", "qpass", "tree", "cert"),
+                    default="pass",
                     help="pass: 64 layers + LM head argmax + tree acceptance at M=32 (the headline line); "
                          "block: the same with one layer; "
                          "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
                          "and 2%% outliers; "
                          "sweep: Wgate|Wup 34816x5120 over M = 1 ... 512; "
                          "qpass: one block + head through the Q pass (8-bit view only) next to the exact pass; "
-                         "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree")
+                         "tree: best-first draft trees, 24 requests sharing 192 rows and one 32-row tree; "
+                         "cert: the certified INT8 LM head next to the W12 head at M=32")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -393,7 +446,7 @@ def main():
     torch.cuda.set_device(dev)
     w12.lib()
     fn = {"pass": run_pass, "block": run_block, "batched": run_batched, "sweep": run_sweep,
-          "qpass": run_qpass, "tree": run_tree}[args.workload]
+          "qpass": run_qpass, "tree": run_tree, "cert": run_cert}[args.workload]
     return fn(args, w12, synth, torch, dev)
 
 

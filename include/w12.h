@@ -183,10 +183,9 @@ w12_status w12_gemm(const w12_matrix *w, const uint16_t *x, int64_t m,
  * loaded and held until the process ends). The call allocates nothing.
  *   Arguments and layouts as w12_gemm, without ws / ws_bytes.
  *   Returns W12_ENOSPC, before launching anything, when w12_gemm_workspace
- *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES. No workspace part grows
- *   with n or k, so at 256 compute units every accepted shape fits (the
- *   largest workspace, 192-row launches, is 51.6 MB); a device with more
- *   than about 330 compute units could exceed it at m > 64.
+ *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES. At 256 compute units
+ *   every m <= 512 fits for k <= 400000 (192-row launches need 51.6 MB;
+ *   16 <= m <= 64 adds 128 * k bytes of x fragments).
  *   The first call on a device looks up the array's device address and
  *   enqueues one kernel on `stream` that zero-fills it; every completed call
  *   leaves its counters at zero again.
@@ -210,6 +209,66 @@ w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t *by
 w12_status w12_head_argmax(const w12_matrix *head, const uint16_t *x, int64_t m,
                            int32_t *idx, float *maxval, void *ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * Certified INT8 LM head ([S1] 4.1, the LM-head paragraph: an INT8 copy of
+ * the head, a per-row Cauchy-Schwarz error bound that proves which tokens
+ * cannot be the argmax, exact rescoring of the survivors only; the argmax
+ * does not change).
+ *
+ * The INT8 copy of an n x k head (device memory, caller-owned):
+ *   q       [n*k] int8: per vocabulary row and block of 32 consecutive k,
+ *           every weight the W12 pack keeps in its window is
+ *           q = RNE(w / 2^s), s the smallest integer with all of the
+ *           block's window weights |w| <= 127 * 2^s; weights W12 escapes
+ *           are 0 (they come back exactly from the W12 head's escape
+ *           list). Layout: 8 KB records, record (strip, r) at
+ *           (strip*(k/256) + r) * 8192, weight (c, k') at the byte W12's
+ *           8-bit view uses: t*1024 + (c + 32h)*16 + j.
+ *   qexp    [n*k/32] u8 block codes s + 133 (0: no window weight in the
+ *           block) at ((strip*(k/256) + r)*8 + t)*32 + c.
+ *   cbound  [n] fp32 per-row constant ||e|| + 2 k 2^-24 ||w'||, rounded up
+ *           (w' = the copy's weights with the escapes exact, e = w - w').
+ */
+typedef struct w12_cert8 {
+  int64_t n, k;
+  const int8_t *q;
+  const uint8_t *qexp;
+  const float *cbound;
+} w12_cert8;
+
+/* w12_cert8_pack -- build the INT8 copy from the bf16 head w [n, k] and the
+ * window tops e_top [n] that w12_pack_plan gave for the same w (load time).
+ * q, qexp, cbound as above (q 16-byte aligned, cbound 4-byte aligned). */
+w12_status w12_cert8_pack(const uint16_t *w, int64_t n, int64_t k, const uint8_t *e_top,
+                          int8_t *q, uint8_t *qexp, float *cbound, hipStream_t stream);
+
+/* Workspace bytes w12_head_argmax_certified needs (host output). */
+w12_status w12_head_argmax_certified_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
+
+/*
+ * w12_head_argmax_certified -- the certified head argmax for 1 <= m <= 64
+ * rows: an MFMA pass over the INT8 copy gives A = x.w' (fp32) per row and
+ * vocabulary row, with bounds A +- B, B = ||x|| cbound + 1e-6 (rounded
+ * outward); LB = the row's largest lower bound; every group of 4 vocabulary
+ * rows whose upper bound reaches LB is rescored exactly from the W12 head
+ * (its records and escapes, fp32 accumulation). idx[i] = the lowest id
+ * attaining the largest rescored logit, which is the exact head argmax
+ * (within the same floating-point allowance as w12_head_argmax).
+ *   head    the W12 head of the same weights; cert its INT8 copy (same n, k).
+ *   idx     [m] int32 out; maxval [m] fp32 out or NULL (the winning logit);
+ *   rescored [m] int32 out or NULL: vocabulary rows rescored per row.
+ *   ws      zero-filled workspace of >= w12_head_argmax_certified_workspace
+ *           bytes; every completed call leaves its counters and keys at
+ *           zero again, so one workspace serves certified calls of any
+ *           shape (but not w12_gemm / w12_head_argmax calls: their
+ *           counters sit at other offsets).
+ * Errors: W12_EINVAL also when one workgroup's share of the head spans more
+ * than 4096 vocabulary rows (n above about 900000 at 256 compute units).
+ */
+w12_status w12_head_argmax_certified(const w12_matrix *head, const w12_cert8 *cert, const uint16_t *x,
+                                     int64_t m, int32_t *idx, float *maxval, int32_t *rescored,
+                                     void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * w12_gemm_qpass, w12_head_argmax_qpass -- the Q pass ([S1] 4.3): the same

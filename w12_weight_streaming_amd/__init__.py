@@ -39,6 +39,11 @@ class W12Matrix(ctypes.Structure):
                 ("esc_off", ctypes.c_void_p), ("esc", ctypes.c_void_p)]
 
 
+class W12Cert8(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("qexp", ctypes.c_void_p), ("cbound", ctypes.c_void_p)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libw12.so; raises if it has not been built."""
     global _lib
@@ -64,6 +69,10 @@ def lib() -> ctypes.CDLL:
             "w12_head_argmax": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "w12_gemm_qpass": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp, sz, vp]),
             "w12_gemm_noalloc": (ctypes.c_int, [mp, vp, i64, vp, ctypes.c_int, vp]),
+            "w12_cert8_pack": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, vp]),
+            "w12_head_argmax_certified_workspace": (ctypes.c_int, [i64, i64, i64, ctypes.POINTER(sz)]),
+            "w12_head_argmax_certified": (ctypes.c_int, [mp, ctypes.POINTER(W12Cert8), vp, i64, vp, vp, vp, vp,
+                                                         sz, vp]),
             "w12_head_argmax_qpass": (ctypes.c_int, [mp, vp, i64, vp, vp, vp, sz, vp]),
             "tree_accept": (ctypes.c_int, [i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "w12_tree_build_workspace": (ctypes.c_int, [i32, i32, ctypes.POINTER(sz)]),
@@ -83,7 +92,8 @@ def exported_symbols():
             "w12_decode", "w12_check", "w12_gemm_workspace", "w12_gemm",
             "w12_head_argmax_workspace", "w12_head_argmax", "w12_gemm_qpass",
             "w12_head_argmax_qpass", "tree_accept", "w12_tree_build_workspace", "w12_tree_build",
-            "w12_gemm_noalloc"]
+            "w12_gemm_noalloc", "w12_cert8_pack", "w12_head_argmax_certified_workspace",
+            "w12_head_argmax_certified"]
 
 
 def _ok(status: int, what: str):
@@ -280,6 +290,62 @@ def w12_head_argmax(pw: PackedW12, x: torch.Tensor, ws: torch.Tensor | None = No
     _ok(fn(ctypes.byref(d), _ptr(x), m, _ptr(idx), _ptr(mx), _ptr(ws), ws.numel(),
            _stream(x.device)), name)
     return idx, mx
+
+
+@dataclass
+class Cert8Head:
+    """Device-resident INT8 copy of an LM head for the certified argmax."""
+    n: int
+    k: int
+    q: torch.Tensor        # int8 [n*k], 8 KB records
+    qexp: torch.Tensor     # uint8 [n*k/32] block scale codes
+    cbound: torch.Tensor   # float32 [n] per-row bound constants
+
+    def desc(self) -> W12Cert8:
+        return W12Cert8(self.n, self.k, self.q.data_ptr(), self.qexp.data_ptr(), self.cbound.data_ptr())
+
+    def nbytes(self) -> int:
+        return self.q.numel() + self.qexp.numel() + 4 * self.cbound.numel()
+
+
+def w12_cert8_pack(w: torch.Tensor, pw: PackedW12) -> Cert8Head:
+    """INT8 copy of the bf16 head w [n, k], using the window tops of its
+    W12 pack pw (the weights W12 escapes are left to its escape list)."""
+    _need(w, torch.bfloat16, "w", 2)
+    n, k = w.shape
+    if (n, k) != (pw.n, pw.k):
+        raise ValueError("w and its W12 pack differ in shape")
+    dev = w.device
+    q = torch.empty(n * k, dtype=torch.int8, device=dev)
+    qexp = torch.empty(n * k // 32, dtype=torch.uint8, device=dev)
+    cb = torch.empty(n, dtype=torch.float32, device=dev)
+    _ok(lib().w12_cert8_pack(_ptr(w), n, k, _ptr(pw.e_top), _ptr(q), _ptr(qexp), _ptr(cb), _stream(dev)),
+        "w12_cert8_pack")
+    return Cert8Head(n, k, q, qexp, cb)
+
+
+def w12_head_argmax_certified(pw: PackedW12, cert: Cert8Head, x: torch.Tensor, ws: torch.Tensor | None = None,
+                              with_max: bool = True):
+    """Certified head argmax of 1 <= m <= 64 rows: (idx int32 [m], max
+    logit float32 [m] or None, rescored vocabulary rows int32 [m])."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if k != pw.k or (cert.n, cert.k) != (pw.n, pw.k):
+        raise ValueError("x, the head and its INT8 copy must agree in shape")
+    dev = x.device
+    idx = torch.empty(m, dtype=torch.int32, device=dev)
+    mx = torch.empty(m, dtype=torch.float32, device=dev) if with_max else None
+    cnt = torch.empty(m, dtype=torch.int32, device=dev)
+    need = ctypes.c_size_t(0)
+    _ok(lib().w12_head_argmax_certified_workspace(pw.n, pw.k, m, ctypes.byref(need)),
+        "w12_head_argmax_certified_workspace")
+    if ws is None:
+        ws = workspace(need.value, dev, "cert")
+    d, c = pw.desc(), cert.desc()
+    _ok(lib().w12_head_argmax_certified(ctypes.byref(d), ctypes.byref(c), _ptr(x), m, _ptr(idx), _ptr(mx),
+                                        _ptr(cnt), _ptr(ws), ws.numel(), _stream(dev)),
+        "w12_head_argmax_certified")
+    return idx, mx, cnt
 
 
 def tree_accept(node_off: torch.Tensor, parent: torch.Tensor, token: torch.Tensor,

@@ -109,6 +109,36 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
   return W12_OK;
 }
 
+// Workspace of the certified head. What must be zero between calls sits at
+// the same offsets for every shape, so one workspace serves calls of any
+// shape: the rescoring's keys, done counter and per-row counts first, then
+// the INT8 pass's GEMM workspace (its own counters at its start; its
+// argmax-key region holds the rows' lower bounds); what every call writes
+// before it reads follows: row norms, then the upper bounds per 4-row group
+// and row.
+struct CertLayout {
+  w12::GemmPlan pl;
+  size_t off_keys2, off_done2, off_list_count, off_counts, off_xnorm, off_gemm, off_u4, off_list, total;
+};
+CertLayout cert_layout(int64_t n, int64_t k, int64_t m, int cu) {
+  CertLayout L{};
+  L.pl = w12::plan_gemm(n, k, m, cu);
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  L.off_keys2 = 0;
+  L.off_done2 = size_t(8) * 8 * 256 * 16;
+  L.off_list_count = L.off_done2 + 128;  // its own cache line
+  L.off_counts = L.off_done2 + 256;
+  L.off_xnorm = L.off_counts + 256;
+  L.off_gemm = L.off_xnorm + 256;
+  // the INT8 pass runs the MFMA kernel for every m, so its x fragments need
+  // ceil(m / 32) tiles even below 16 rows (where plan_gemm reserves none)
+  const size_t xf_end = L.pl.off_xf + (size_t)((m + 31) / 32) * 32 * (size_t)k * 2;
+  L.off_u4 = up(L.off_gemm + (L.pl.ws_bytes > xf_end ? L.pl.ws_bytes : xf_end));
+  L.off_list = up(L.off_u4 + (size_t)(n / 4) * w12::kCertMaxRows * 4);
+  L.total = L.off_list + (size_t)(n / 4) * w12::kCertMaxRows * 8;
+  return L;
+}
+
 w12_status gemm_entry(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, int ytype,
                       void* ws, size_t ws_bytes, hipStream_t stream, bool qpass) {
   if (!matrix_ok(w) || !x || !y || m < 1 || m > kMaxRows) return W12_EINVAL;
@@ -275,6 +305,78 @@ w12_status w12_head_argmax_workspace(int64_t n, int64_t k, int64_t m, size_t* by
 w12_status w12_head_argmax(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,
                            float* maxval, void* ws, size_t ws_bytes, hipStream_t stream) {
   return head_entry(head, x, m, idx, maxval, ws, ws_bytes, stream, false);
+}
+
+w12_status w12_cert8_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, int8_t* q,
+                          uint8_t* qexp, float* cbound, hipStream_t stream) {
+  if (!w || !e_top || !q || !qexp || !cbound || !shape_ok(n, k)) return W12_EINVAL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(cbound, 4)) return W12_EINVAL;
+  return st(w12::launch_cert_pack(w, n, k, e_top, q, qexp, cbound, stream));
+}
+
+w12_status w12_head_argmax_certified_workspace(int64_t n, int64_t k, int64_t m, size_t* bytes) {
+  if (!bytes || !shape_ok(n, k) || m < 1 || m > w12::kCertMaxRows) return W12_EINVAL;
+  const int cu = num_cu();
+  if (cu <= 0) return W12_EHIP;
+  *bytes = cert_layout(n, k, m, cu).total;
+  return W12_OK;
+}
+
+w12_status w12_head_argmax_certified(const w12_matrix* head, const w12_cert8* cert, const uint16_t* x, int64_t m,
+                                     int32_t* idx, float* maxval, int32_t* rescored, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!matrix_ok(head) || !cert || !x || !idx || !ws || m < 1 || m > w12::kCertMaxRows) return W12_EINVAL;
+  if (cert->n != head->n || cert->k != head->k || !cert->q || !cert->qexp || !cert->cbound) return W12_EINVAL;
+  if (!aligned(cert->q, 16) || !aligned(cert->qexp, 4) || !aligned(cert->cbound, 16) || !aligned(x, 16) ||
+      !aligned(ws, 256))
+    return W12_EINVAL;
+  const int cu = num_cu();
+  if (cu <= 0) return W12_EHIP;
+  const CertLayout L = cert_layout(head->n, head->k, m, cu);
+  if (w12::plan_slice_channels(L.pl, head->k) > w12::kCertCbFloats) return W12_EINVAL;
+  if (ws_bytes < L.total) return W12_ENOSPC;
+  char* base = static_cast<char*>(ws);
+  w12::GemmParams p{};
+  p.w = args_of(head);
+  p.x = x;
+  p.M = (int)m;
+  p.N = (int)head->n;
+  p.K = (int)head->k;
+  p.RK = (int)(head->k / 256);
+  p.S = (int)(head->n / 32);
+  p.P = L.pl.P;
+  p.U = L.pl.U;
+  p.G = L.pl.G;
+  p.nq = L.pl.nq;
+  char* gbase = base + L.off_gemm;
+  p.part = reinterpret_cast<float*>(gbase + L.pl.off_part);
+  p.xf = reinterpret_cast<uint4*>(gbase + L.pl.off_xf);
+  p.tile_cnt = reinterpret_cast<uint32_t*>(gbase + L.pl.off_cnt);
+  p.keys = reinterpret_cast<unsigned long long*>(gbase + L.pl.off_keys);
+  p.done = reinterpret_cast<uint32_t*>(gbase + L.pl.off_done);
+  p.cq = cert->q;
+  p.cexp = cert->qexp;
+  p.cbound = cert->cbound;
+  p.xnorm = reinterpret_cast<float*>(base + L.off_xnorm);
+  p.u4 = reinterpret_cast<float*>(base + L.off_u4);
+  w12_status r = st(w12::launch_cert_pass(p, stream));
+  if (r != W12_OK) return r;
+  w12::CertRescoreArgs a{};
+  a.w = p.w;
+  a.x = x;
+  a.M = (int)m;
+  a.K = (int)head->k;
+  a.u4 = p.u4;
+  a.lb_keys = p.keys;
+  a.keys = reinterpret_cast<unsigned long long*>(base + L.off_keys2);
+  a.done = reinterpret_cast<uint32_t*>(base + L.off_done2);
+  a.counts = reinterpret_cast<uint32_t*>(base + L.off_counts);
+  a.list_count = reinterpret_cast<uint32_t*>(base + L.off_list_count);
+  a.list = reinterpret_cast<uint2*>(base + L.off_list);
+  a.idx = idx;
+  a.maxval = maxval;
+  a.rescored = rescored;
+  return st(w12::launch_cert_rescore(a, 2 * cu, stream));
 }
 
 w12_status w12_head_argmax_qpass(const w12_matrix* head, const uint16_t* x, int64_t m, int32_t* idx,

@@ -267,6 +267,33 @@ __device__ __forceinline__ int partial_slot(int g, int p, int U, int G, int RK) 
   return (p == chunk_begin(g, U, G) / RK) ? 2 * g : 2 * g + 1;
 }
 
+// Certified head (INT8 pass): B = ||x|| c + 1e-6 for a row norm xn and a
+// channel's bound constant c, rounded up; then the group of 4 channels
+// n .. n+3 of row m gets its upper bound max (A + B) stored (rounded up) and
+// yields its lower bound max (A - B) (rounded down) as a key (value key, all
+// ones), maximised over the 16 threads of the DPP row; 0 when not valid.
+__device__ __forceinline__ float cert_bound(float xn, float c) {
+  const float p = xn * c;
+  return fmaf(p, 0x1p-22f, p) + 1.0001e-6f;
+}
+__device__ __forceinline__ unsigned long long cert_emit4(const GemmParams& a, int m, int n, float4 v, float4 cb,
+                                                         float xn) {
+  unsigned long long best = 0;
+  if (m < a.M && n < a.N) {
+    const float vv[4] = {v.x, v.y, v.z, v.w}, cc[4] = {cb.x, cb.y, cb.z, cb.w};
+    float up = -__builtin_huge_valf(), lo = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float B = cert_bound(xn, cc[i]), slack = (fabsf(vv[i]) + B) * 0x1p-22f;
+      up = fmaxf(up, (vv[i] + B) + slack);
+      lo = fmaxf(lo, (vv[i] - B) - slack);
+    }
+    a.u4[(size_t)(n >> 2) * kCertMaxRows + m] = up;
+    best = ((unsigned long long)float_key(lo) << 32) | 0xFFFFFFFFull;
+  }
+  return row16_max(best);
+}
+
 // Last contributor of a split tile sums the partials in slice order. Called
 // after writes_done_barrier(), once per split tile of the slice. NT threads,
 // TC channels per tile, CH float4 per thread per round; 16 consecutive
@@ -318,10 +345,17 @@ __device__ __forceinline__ void finish_split_tile(const GemmParams& a, int p, in
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const int e = e0 + j * NT + tid;
-        if constexpr (EPI == kEpiArgmax) {
+        if constexpr (EPI == kEpiArgmax || EPI == kEpiCert) {
           // Q consecutive threads hold one row: maximise over all of them
           // (Q <= 64, one wave) before the one atomic of the row
-          unsigned long long key = row_key4(a, e / Q, p * TC + (e % Q) * 4, v[j]);
+          unsigned long long key;
+          if constexpr (EPI == kEpiCert) {
+            const int m = e / Q, n = p * TC + (e % Q) * 4;
+            const float4 cb = n < a.N ? *reinterpret_cast<const float4*>(a.cbound + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+            key = cert_emit4(a, m, n, v[j], cb, m < a.M ? a.xnorm[m] : 0.f);
+          } else {
+            key = row_key4(a, e / Q, p * TC + (e % Q) * 4, v[j]);
+          }
           if constexpr (Q >= 32) key = kmax(key, shfl_xor64(key, 16));
           if constexpr (Q >= 64) key = kmax(key, shfl_xor64(key, 32));
           if ((e % Q) == 0 && key) atomicMax(key_slot(a, e / Q), key);
@@ -400,11 +434,30 @@ __device__ __forceinline__ void patch_put(char* buf, uint32_t e) {
   *reinterpret_cast<uint16_t*>(buf + at) = esc_bits(e);
 }
 
+// The certified head's INT8 copy: the lane's 16 codes q (one 16-byte load,
+// the same place a W12 record keeps the 8-bit view) and its block's scale
+// code (s + 133; 0 when the block has no window weight, then every q is 0)
+// give the bf16 pairs q * 2^s, exact: |q| <= 127 has at most 7 significant
+// bits, so the binary32 value q * 2^s keeps its low 16 bits zero.
+__device__ __forceinline__ void cert_decode16(const uint4 hi, uint32_t code, uint32_t (&p)[8]) {
+  const int sig = code ? (int)code - 133 : 0;
+  const uint32_t d[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t word = d[i >> 1];
+    const int sh = 16 * (i & 1);
+    const float f0 = __builtin_amdgcn_ldexpf((float)(int)(int8_t)(word >> sh), sig);
+    const float f1 = __builtin_amdgcn_ldexpf((float)(int)(int8_t)(word >> (sh + 8)), sig);
+    p[i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+}
+
 // Restore the lane's NQ x 16 weights of a unit (one subtile of each strip of
 // the tile) and apply the escape blocks' entries: the restored pairs go to the
 // wave's LDS patch buffer (2 KB per strip), the lanes holding entries overwrite
 // their slots, the pairs are read back. Only the wave itself touches its buffer.
-template <int NQ, typename SlotT>
+// For the INT8 copy, bias[q] is the lane's block scale code instead.
+template <int NQ, int FMT = kFmtW12, typename SlotT>
 __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bias)[NQ], char* patch,
                                              uint32_t plo, int lane, rsrc_t r_esc, uint32_t (&P)[NQ][8]) {
   int cq[NQ];
@@ -418,8 +471,13 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
     any |= cq[q];
   }
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
-    decode16(uint4{s.hi[q].x, s.hi[q].y, s.hi[q].z, s.hi[q].w}, uint2{s.lo[q].x, s.lo[q].y}, bias[q], P[q]);
+  for (int q = 0; q < NQ; ++q) {
+    if constexpr (FMT == kFmtCert8) {
+      cert_decode16(uint4{s.hi[q].x, s.hi[q].y, s.hi[q].z, s.hi[q].w}, bias[q], P[q]);
+    } else {
+      decode16(uint4{s.hi[q].x, s.hi[q].y, s.hi[q].z, s.hi[q].w}, uint2{s.lo[q].x, s.lo[q].y}, bias[q], P[q]);
+    }
+  }
   if (any > 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) patch_store(patch + q * 2048, plo, P[q]);
@@ -509,11 +567,18 @@ constexpr uint32_t kMidNibbles = 0x88888888u;
 //    covers the n_esc entries; lanes past the block's count are not used.
 constexpr uint32_t kOutOfRange = 1u << 30;
 
-template <int XQ, bool QP, int NQ>
+// FMT = kFmtCert8 streams the certified head's INT8 copy instead: 8 KB
+// records (the 8-bit-view plane layout, no low nibbles) and, in place of
+// the window tops, the dword of block scale codes around the lane's channel
+// (code (strip, record, subtile, channel) at byte ((strip * RK + record) * 8
+// + subtile) * 32 + channel). Escapes come from the W12 head's lists.
+template <int XQ, bool QP, int NQ, int FMT = kFmtW12>
 struct UnitLoads {
+  static constexpr bool kCert = FMT == kFmtCert8;
+  static constexpr uint32_t kStep = kCert ? (uint32_t)kCertRecBytes : (uint32_t)kRecBytes;
   const GemmParams& a;
   int wave, RK, S, u1;
-  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4;
+  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4, sb_strip;
   rsrc_t r_esc, r_off, r_et;
   const void* x_base;
   uint32_t x_bytes, x_tile, x_step;
@@ -529,7 +594,8 @@ struct UnitLoads {
                                        const void* xb, uint32_t xbytes, uint32_t xtile, uint32_t xstep)
       : a(a_), wave(wave_), RK(a_.RK), S(a_.S), u1(u1_), x_base(xb), x_bytes(xbytes), x_tile(xtile),
         x_step(xstep) {
-    strip_bytes = (uint32_t)RK * kRecBytes;
+    strip_bytes = (uint32_t)RK * kStep;
+    sb_strip = kCert ? (uint32_t)RK * 256u : (uint32_t)kStrip;
     v_hi = (uint32_t)(wave * 1024 + lane * 16);
     v_lo = (uint32_t)(kHiBytes + wave * 512 + lane * 8);
     v_l4 = (uint32_t)lane * 4u;
@@ -538,7 +604,11 @@ struct UnitLoads {
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
     r_off = make_rsrc(a.w.esc_off, (uint32_t)(a.w.nb + 1) * 4u);
-    r_et = make_rsrc(a.w.e_top, (uint32_t)a.w.n);
+    if constexpr (kCert) {
+      r_et = make_rsrc(a.cexp, (uint32_t)(a.w.n * a.w.k / 32));
+    } else {
+      r_et = make_rsrc(a.w.e_top, (uint32_t)a.w.n);
+    }
     const int p = u0 / RK, r = u0 - p * RK;
     w = StreamPos{u0, min(RK - r, u1 - u0), p};
     w_tile(r);
@@ -550,19 +620,27 @@ struct UnitLoads {
   __device__ __forceinline__ void w_tile(int r) {
     const int sq = NQ * w.p;
     const int ns = min(NQ, S - sq);
-    rt = make_rsrc(a.w.rec + (int64_t)sq * strip_bytes, (uint32_t)ns * strip_bytes);
+    rt = make_rsrc(rec_base() + (int64_t)sq * strip_bytes, (uint32_t)ns * strip_bytes);
     rx = make_rsrc(x_base, x_bytes);
-    so = (uint32_t)r * kRecBytes;
+    so = (uint32_t)r * kStep;
     sx = x_tile + (uint32_t)r * x_step;
-    sb = (uint32_t)sq * kStrip;
+    sb = kCert ? (uint32_t)(((sq * RK + r) * 8 + wave) * 32) : (uint32_t)sq * kStrip;
+  }
+  __device__ __forceinline__ const uint8_t* rec_base() const {
+    if constexpr (kCert) {
+      return reinterpret_cast<const uint8_t*>(a.cq);
+    } else {
+      return a.w.rec;
+    }
   }
   __device__ __forceinline__ void w_next() {
     ++w.u;
-    so += kRecBytes;
+    so += kStep;
     sx += x_step;
+    if constexpr (kCert) sb += 256u;  // the next record's codes
     if (--w.left == 0) {
       if (w.u >= u1) {  // past the slice
-        rt = make_rsrc(a.w.rec, 0u);
+        rt = make_rsrc(rec_base(), 0u);
         rx = rt;
         w.left = 1 << 30;
       } else {
@@ -598,14 +676,14 @@ struct UnitLoads {
     for (int q = 0; q < NQ; ++q) {
       const uint32_t sq = so + (uint32_t)q * strip_bytes;
       s.hi[q] = bload4<kNonTemporal>(rt, v_hi, sq);
-      if constexpr (QP) {
+      if constexpr (QP || kCert) {
         s.lo[q] = u32x2{kMidNibbles, kMidNibbles};
       } else {
         s.lo[q] = bload2<kNonTemporal>(rt, v_lo, sq);
       }
       // a whole dword: a byte load's result would be widened where the ring
       // wraps round, which makes the compiler wait for the load right there
-      s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * kStrip);
+      s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * sb_strip);
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
@@ -668,8 +746,9 @@ __device__ __forceinline__ uint32_t bias2_of_top(uint32_t et4, int lane) {
 
 // ============================================================================ MFMA path (m >= 16)
 
-template <int MT, int EPI, bool QP, int NQ>
+template <int MT, int EPI, bool QP, int NQ, int FMT = kFmtW12>
 __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
+  static_assert((FMT == kFmtCert8) == (EPI == kEpiCert), "the INT8 copy runs the bound epilogue");
   // x fragments of the MT tiles of 32 rows ride in the load ring.
   static_assert(MT >= 1 && MT <= 2, "small-m kernel: at most 64 rows");
   constexpr int XQ = MT;
@@ -682,6 +761,8 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   constexpr int SF = 32 * RS;           // reduction slot (one wave, one M-tile)
   __shared__ __align__(16) float lds[kNW * SF];  // reduction slots; patch buffers alias them
   __shared__ int s_last;
+  // INT8 pass: the bound constants of the channels of the slice's tiles
+  __shared__ __align__(16) float cbl[FMT == kFmtCert8 ? kCertCbFloats : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -704,10 +785,26 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
   // x fragment (record r, subtile t, tile mt, half h) of the fragment buffer
   // is at ((r * 8 + t) * MT + mt) * 2048 + h * 1024.
-  UnitLoads<XQ, QP, NQ> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
-                      (uint32_t)(wave * MT * 2048), (uint32_t)(MT * 8 * 2048));
+  UnitLoads<XQ, QP, NQ, FMT> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
+                               (uint32_t)(wave * MT * 2048), (uint32_t)(MT * 8 * 2048));
   const uint32_t plo = patch_lane_off(lane);
   const uint32_t v_x = (uint32_t)lane * 16u;
+
+  // INT8 pass: the thread's row norms, and the slice's channel constants in
+  // LDS (the host checks that they fit; the first tile end's barrier orders
+  // these writes before any read)
+  float xn[MT];
+  int ch0 = 0;
+  if constexpr (FMT == kFmtCert8) {
+    ch0 = (u0 / RK) * TC;
+    const int ch1 = u0 < u1 ? min(((u1 - 1) / RK + 1) * TC, a.N) : ch0;
+    for (int i = tid; i < ch1 - ch0; i += kNT) cbl[i] = a.cbound[ch0 + i];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 32 + (tid >> 4);
+      xn[mt] = m < a.M ? a.xnorm[m] : 0.f;
+    }
+  }
 
   auto issue_x = [&](Slot<XQ, NQ>& s) __attribute__((always_inline)) {
 #pragma unroll
@@ -753,6 +850,9 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
         if (whole) {
           if constexpr (EPI == kEpiArgmax) {
             run[mt] = kmax(run[mt], row_key4(a, m, p * TC + c4, v));
+          } else if constexpr (EPI == kEpiCert) {
+            const float4 cb = *reinterpret_cast<const float4*>(cbl + (p * TC + c4 - ch0));
+            run[mt] = kmax(run[mt], cert_emit4(a, m, p * TC + c4, v, cb, xn[mt]));
           } else {
             emit4<EPI>(a, tid, m, p * TC + c4, v);
           }
@@ -782,9 +882,15 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     ++cur.u;
     uint32_t bias[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) bias[q] = bias2_of_top(s.et[q], lane);
+    for (int q = 0; q < NQ; ++q) {
+      if constexpr (FMT == kFmtCert8) {
+        bias[q] = __builtin_amdgcn_ubfe(s.et[q], 8u * (uint32_t)(lane & 3), 8);  // block scale code
+      } else {
+        bias[q] = bias2_of_top(s.et[q], lane);
+      }
+    }
     uint32_t P[NQ][8];
-    restore_unit<NQ>(s, bias, patch, plo, lane, L.r_esc, P);
+    restore_unit<NQ, FMT>(s, bias, patch, plo, lane, L.r_esc, P);
     const u32x4 (&xl)[MT][2] = s.xv;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -802,7 +908,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
     walk_slice<XQ, NQ, D>(L, u0, u1, issue_x, step);
     flush(cur.p);
   }
-  if constexpr (EPI == kEpiArgmax) {
+  if constexpr (EPI == kEpiArgmax || EPI == kEpiCert) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       if ((tid & 15) == 0 && run[mt]) atomicMax(key_slot(a, mt * 32 + (tid >> 4)), run[mt]);
@@ -1335,6 +1441,54 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__
   xf[c] = v;
 }
 
+// Certified head: x fragments as xfrag_kernel (blocks [0, fb)), and in the
+// blocks after them one wavefront per row m < M computing ||x_m|| -- the
+// squares summed in fp64 (exact for bf16) in a fixed order, the root rounded
+// up to binary32.
+__global__ __launch_bounds__(256) void cert_prep_kernel(const uint16_t* __restrict__ x, int M, int K, int MT,
+                                                        uint4* __restrict__ xf, int fb, float* __restrict__ xnorm) {
+  if ((int)blockIdx.x < fb) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int total = (K / 32) * MT * 128;
+    if (c >= total) return;
+    const int l = c & 63, i = (c >> 6) & 1, bm = c >> 7;
+    const int mt = bm % MT, b = bm / MT;
+    const int m = mt * 32 + (l & 31);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + b * 32 + 16 * (l >> 5) + 8 * i);
+    xf[c] = v;
+    return;
+  }
+  // one workgroup per row: every thread sums its 16-byte pieces, then a
+  // fixed-order reduction over the workgroup
+  __shared__ double part[256];
+  const int m = (int)blockIdx.x - fb, tid = threadIdx.x;
+  if (m >= M) return;
+  const uint4* row = reinterpret_cast<const uint4*>(x + (int64_t)m * K);
+  double acc = 0.0;
+  for (int i = tid; i < K / 8; i += 256) {
+    const uint4 v = row[i];
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = (double)__uint_as_float(d[j] << 16), hi = (double)__uint_as_float(d[j] & 0xFFFF0000u);
+      acc += lo * lo + hi * hi;
+    }
+  }
+  part[tid] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) part[tid] += part[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double r = sqrt(part[0]) * (1.0 + 0x1p-40);
+    float f = (float)r;
+    if ((double)f < r) f = __uint_as_float(__float_as_uint(f) + 1u);
+    xnorm[m] = f;
+  }
+}
+
 // ============================================================================ dispatch
 
 struct KernelSel {
@@ -1385,7 +1539,7 @@ constexpr size_t kCounterBytes = size_t(4) << 18;              // u32 per tile, 
 constexpr size_t kKeyBytes = size_t(8) * kKeyCopies * kKeyRows * kKeyStride;  // argmax keys
 constexpr size_t kStateBytes = kCounterBytes + kKeyBytes + 256;                 // + done counter
 
-GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
+GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq) {
   GemmPlan pl{};
   const bool big = m > kSmallMaxRows;
   const int64_t S = n / kStrip, RK = k / kRecK;
@@ -1393,7 +1547,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   // fragment then serves 4 strips, and tiles end half as often); shorter
   // slices keep 2-strip tiles, whose finer units balance the slices better.
   int nq = 2;
-  if (!big && m >= 16 && m <= 32) {
+  if (!big && m >= 16 && m <= 32 && max_nq >= 4) {
     const int64_t U4 = ((S + 3) / 4) * RK;
     const int64_t G4 = U4 < num_cu ? U4 : num_cu;
     if (U4 >= (int64_t)kNq4MinUnits * G4) nq = 4;
@@ -1422,6 +1576,32 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu) {
   pl.off_xf = (pl.off_part + part_bytes + 255) & ~size_t(255);
   pl.ws_bytes = pl.off_xf + (size_t)mt * 32 * k * 2;
   return pl;
+}
+
+int64_t plan_slice_channels(const GemmPlan& pl, int64_t k) {
+  const int64_t RK = k / kRecK, per = ((int64_t)pl.U + pl.G - 1) / pl.G;
+  const int64_t tiles = 1 + (per + RK - 2) / RK;  // a slice of `per` units starting at any record
+  return tiles * pl.nq * kStrip;
+}
+
+hipError_t launch_cert_pass(const GemmParams& p, hipStream_t s) {
+  const int mt = (p.M + 31) / 32;
+  const int64_t chunks = (int64_t)(p.K / 32) * mt * 128;
+  const int fb = (int)((chunks + 255) / 256);
+  hipLaunchKernelGGL(cert_prep_kernel, dim3(fb + p.M), dim3(256), 0, s, p.x, p.M, p.K, mt, p.xf, fb,
+                     const_cast<float*>(p.xnorm));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const void* fn = nullptr;
+  if (mt == 1) {
+    fn = p.nq == 4 ? reinterpret_cast<const void*>(&gemm_mfma_kernel<1, kEpiCert, false, 4, kFmtCert8>)
+                   : reinterpret_cast<const void*>(&gemm_mfma_kernel<1, kEpiCert, false, 2, kFmtCert8>);
+  } else if (mt == 2 && p.nq == 2) {
+    fn = reinterpret_cast<const void*>(&gemm_mfma_kernel<2, kEpiCert, false, 2, kFmtCert8>);
+  }
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  return hipLaunchKernel(fn, dim3(p.G), dim3(kNT), args, 0, s);
 }
 
 hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s) {

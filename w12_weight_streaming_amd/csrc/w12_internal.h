@@ -14,7 +14,18 @@ struct MatrixArgs {
   int64_t n, k, nb;
 };
 
-enum Epilogue { kEpiY = 0, kEpiArgmax = 1 };
+enum Epilogue { kEpiY = 0, kEpiArgmax = 1, kEpiCert = 2 };
+
+// Weight formats the small-m MFMA kernel streams: W12 records, or the
+// certified head's INT8 copy (8 KB records laid out as W12's 8-bit-view
+// plane, one scale code per 32-k block of a channel, W12's escapes).
+enum Format { kFmtW12 = 0, kFmtCert8 = 1 };
+constexpr int kCertRecBytes = 8192;
+// floats of per-channel bound constants a workgroup of the INT8 pass keeps
+// in LDS (the channels of its slice's tiles)
+constexpr int kCertCbFloats = 4096;
+// rows of the certified head (one MFMA path, at most two 32-row tiles)
+constexpr int kCertMaxRows = 64;
 
 // Rows up to kSmallMaxRows run the small-m kernels (64-channel tiles); more
 // rows, up to kRowsPerLaunch per launch, the large-m kernel (128-channel
@@ -44,7 +55,37 @@ struct GemmParams {
   uint32_t* done;         // [1] finished-workgroup counter, zero between calls
   int32_t* idx;
   float* maxval;
+  // certified head's INT8 pass (kEpiCert): the copy, the bound constants,
+  // the row norms of x, and the upper bounds per 4-channel group and row
+  const int8_t* cq;
+  const uint8_t* cexp;
+  const float* cbound;
+  const float* xnorm;
+  float* u4;  // [ceil(N / 4)][64]
 };
+
+// Certified head: the INT8 copy's pack, and the rescoring that follows the
+// INT8 pass.
+struct CertRescoreArgs {
+  MatrixArgs w;            // the W12 head (records and escapes for the exact logits)
+  const uint16_t* x;
+  int M, K;
+  const float* u4;         // [ceil(N / 4)][64] upper bounds
+  unsigned long long* lb_keys;  // per-row lower bounds (argmax key layout), cleared at the end
+  unsigned long long* keys;     // exact argmax keys (same layout), cleared at the end
+  uint32_t* done;
+  uint32_t* counts;        // [64] rescored vocabulary rows per input row, cleared at the end
+  uint32_t* list_count;    // entries the selection listed, cleared at the end
+  uint2* list;             // [N / 4 * 64] entries (group, row)
+  int32_t* idx;
+  float* maxval;
+  int32_t* rescored;
+};
+hipError_t launch_cert_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* e_top, int8_t* q,
+                            uint8_t* code, float* cbound, hipStream_t s);
+// the selection (groups whose upper bound reaches a row's lower bound) and
+// the exact rescoring of the selected groups (rescore_grid workgroups)
+hipError_t launch_cert_rescore(const CertRescoreArgs& a, int rescore_grid, hipStream_t s);
 
 struct GemmPlan {
   int G, U, P;
@@ -54,11 +95,19 @@ struct GemmPlan {
 };
 
 // Plan of one launch (m <= kRowsPerLaunch).
-GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu);
+GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq = 4);
 
 // qpass: read only the 8-bit view of the records (low nibbles at their
 // midpoint); escapes are restored as in the exact pass.
 hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s);
+
+// The certified head's INT8 pass (m <= kCertMaxRows): x fragments and row
+// norms, then the MFMA pass over the INT8 copy with the bound epilogue.
+// p.xnorm and p.u4 point into the workspace.
+hipError_t launch_cert_pass(const GemmParams& p, hipStream_t s);
+// Largest number of channels one workgroup's slice covers in a plan (the
+// INT8 pass keeps their bound constants in LDS).
+int64_t plan_slice_channels(const GemmPlan& pl, int64_t k);
 
 hipError_t launch_pack_plan(const uint16_t* w, int64_t n, int64_t k, uint8_t* e_top,
                             uint32_t* esc_off, hipStream_t s);
