@@ -67,13 +67,20 @@ def test_noalloc_equals_gemm_on_two_calls(w12, n, k, m1, m2):
             assert V.within_tolerance(got.cpu().numpy(), y_ref, bound).all()
 
 
-def test_noalloc_scratch_holds_every_workspace(w12):
-    """The scratch array holds the workspace of every shape the library
-    accepts on this device (rows up to 512 run as launches of at most 192,
-    and no workspace part grows with k), so no call is refused for size.
-    Only the size queries run here: nothing is launched."""
-    worst = 0
-    for n, k in ((32, 256), (152064, 5120), (5120, 17408), (2048, 1 << 20), (1 << 21, 1024)):
-        for m in (1, 16, 32, 33, 64, 65, 192, 193, 512):
-            worst = max(worst, w12.gemm_workspace_bytes(n, k, m))
-    assert 0 < worst <= w12.NOALLOC_SCRATCH_BYTES, worst
+def test_noalloc_scratch_fits_the_workloads_and_refuses_beyond(w12):
+    """Every shape of the verify pass, the LM head and the batched case fits
+    the scratch; a shape whose workspace does not (16 <= m <= 64 needs 128 k
+    bytes of x fragments: k = 2^20) is refused with W12_ENOSPC. The refused
+    call is made only after the library's own size query has said that the
+    shape exceeds the scratch, so it cannot reach a launch."""
+    for n, k in ((8192, 5120), (5120, 6144), (34816, 5120), (5120, 17408), (152064, 5120), (17408, 5120)):
+        for m in (1, 16, 32, 64, 192, 512):
+            assert w12.gemm_workspace_bytes(n, k, m) <= w12.NOALLOC_SCRATCH_BYTES, (n, k, m)
+    n, k, m = 2048, 1 << 20, 64
+    assert w12.gemm_workspace_bytes(n, k, m) > w12.NOALLOC_SCRATCH_BYTES
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)  # never read: the size check comes first
+    p = buf.data_ptr()
+    d = w12.W12Matrix(n, k, p, p, p, p)
+    st = w12.lib().w12_gemm_noalloc(ctypes.byref(d), ctypes.c_void_p(p), m, ctypes.c_void_p(p), 0,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == w12.W12_ENOSPC
