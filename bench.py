@@ -410,6 +410,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=LAYERS, help="layers of the pass workload (default 64)")
+    ap.add_argument("--rows", type=int, default=192,
+                    help="verify rows of the batched workload (default 192 = 24 trees x 8 nodes; at most 512)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense bf16 context timing of the same pass")
@@ -420,7 +422,7 @@ def main():
                     default="pass",
                     help="pass: 64 layers + LM head argmax + tree acceptance at M=32 (the headline line); "
                          "block: the same with one layer; "
-                         "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 with 3%% zeros "
+                         "batched: Wup 17408x5120 and Wdown 5120x17408 at M=192 (--rows) with 3%% zeros "
                          "and 2%% outliers; "
                          "sweep: Wgate|Wup 34816x5120 over M = 1 ... 512; "
                          "qpass: one block + head through the Q pass (8-bit view only) next to the exact pass; "
@@ -471,10 +473,13 @@ def time_events(fn, reps):
 
 def run_batched(args, w12, synth, torch, dev):
     """Batched verify (24 trees x 8 nodes = 192 rows): Wup 17408x5120 then
-    Wdown 5120x17408, 3% zeros and 2% x64 outliers, bf16 out. Each matrix is
-    held in enough distinct packed copies (>= 1 GiB in all) that every call
-    streams its weights from HBM, not from the 256 MB last-level cache."""
-    m = 192
+    Wdown 5120x17408, 3% zeros and 2% x64 outliers, bf16 out; --rows sets
+    another row count (every count up to 512 is one launch per matrix). Each
+    matrix is held in enough distinct packed copies (>= 1 GiB in all) that
+    every call streams its weights from HBM, not from the 256 MB last-level
+    cache."""
+    m = args.rows
+    assert 1 <= m <= 512, "--rows must be in [1, 512]"
     mats = []
     for name, n, k, idx in (("UP", FFN, HIDDEN, 1), ("DOWN", HIDDEN, FFN, 2)):
         seed = 1_000_000 * 5 + idx
@@ -506,11 +511,11 @@ def run_batched(args, w12, synth, torch, dev):
     gbps = nbytes / (us * 1e-6) / 1e9
     tflops = flops / (us * 1e-6) / 1e12
     line = {
-        "metric": "W12 batched verify GEMM effective HBM GB/s at M=192 rows",
+        "metric": f"W12 batched verify GEMM effective HBM GB/s at M={m} rows",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "batched verify: Wup 17408x5120 + Wdown 5120x17408, M=192 rows, "
+        "config": {"workload": f"batched verify: Wup 17408x5120 + Wdown 5120x17408, M={m} rows, "
                                "3% zeros + 2% x64 outliers, bf16 out, >= 1 GiB of rotated copies",
                    "rows": m, "bytes_per_step": int(nbytes), "flops_per_step": flops},
         "breakdown_us": {n: round(v, 2) for n, v in per.items()},

@@ -152,7 +152,7 @@ def test_check_detects_corruption(w12):
 
 # (640, 256): one record per strip, so every unit ends a tile
 GEMM_SHAPES = [(1024, 1024), (96, 768), (320, 1792), (640, 256)]
-ROWS = [1, 2, 3, 5, 8, 9, 12, 13, 15, 16, 17, 32, 33, 64, 100, 192, 256, 384, 512]
+ROWS = [1, 2, 3, 5, 8, 9, 12, 13, 15, 16, 17, 32, 33, 64, 100, 130, 192, 256, 300, 384, 450, 512]
 
 
 @pytest.fixture(scope="module")
@@ -202,7 +202,7 @@ def test_gemm_exact_pins(w12, m):
     assert np.array_equal(y2, xi @ wi.T)
 
 
-@pytest.mark.parametrize("m", [1, 16, 32, 64, 100, 192])
+@pytest.mark.parametrize("m", [1, 16, 32, 64, 100, 192, 256, 384, 512])
 def test_gemm_dense_escapes(w12, m):
     """30% exact zeros: ~300 escapes per 1024-weight block, beyond what the
     load ring carries per lane (64 on the small-m path, 128 on the large-m
@@ -281,7 +281,7 @@ def check_argmax(idx, ref_idx, cands):
     return near
 
 
-@pytest.mark.parametrize("m", [1, 5, 12, 15, 16, 32, 48, 100, 192, 256, 512])
+@pytest.mark.parametrize("m", [1, 5, 12, 15, 16, 32, 48, 100, 192, 256, 384, 512])
 def test_head_argmax(w12, m):
     n, k = 8192, 1024
     bits = synth.bits_u16(gen(n, k, 41, p_zero=0.01, p_outlier=0.001))
@@ -579,3 +579,27 @@ def test_four_strip_tiles_with_a_partial_last_tile(w12):
     assert idx.max() < n
     assert np.array_equal(idx, np.argmax(y, axis=1))
     assert np.array_equal(host(mx), y[np.arange(m), idx])
+
+
+# ----------------------------------------------------------------------------- determinism of the hand-off
+
+@pytest.mark.parametrize("n,k,m", [(1024, 1024, 1), (1024, 1024, 12), (5120, 6144, 32), (96, 768, 64),
+                                   (320, 1792, 192), (640, 256, 33), (17408, 5120, 100), (640, 256, 384),
+                                   (5120, 6144, 512)])
+def test_split_tile_hand_off_is_bitwise_repeatable(w12, n, k, m):
+    """Every GEMM path, shapes whose tiles are split between many workgroups
+    (and one record per strip), 20 calls in a row on one workspace: each
+    result equals the first bit for bit (the fixed-order stream-K hand-off),
+    and the head argmax likewise."""
+    say("repeat", n, k, m)
+    w = gen(n, k, 9100 + n + m, p_zero=0.02, p_outlier=0.01, device=DEV)
+    pw = w12.w12_pack(w)
+    x = synth.activations_bf16(m, k, 9200 + m, device=DEV)
+    ws = torch.zeros(w12.gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=DEV)
+    y0 = w12.w12_gemm(pw, x, ws=ws).clone()
+    i0, v0 = (t.clone() for t in w12.w12_head_argmax(pw, x, ws=ws))
+    for rep in range(20):
+        y = w12.w12_gemm(pw, x, ws=ws)
+        assert torch.equal(y, y0), f"GEMM call {rep} differs"
+        i, v = w12.w12_head_argmax(pw, x, ws=ws)
+        assert torch.equal(i, i0) and torch.equal(v, v0), f"argmax call {rep} differs"

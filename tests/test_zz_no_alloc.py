@@ -48,7 +48,7 @@ def noalloc(w12, pw, x, ytype=0):
 # (n, k, first m, second m): the MFMA path (4-strip and 2-strip tiles), the
 # large-m path and the VALU path, each followed by a smaller call
 CASES = [(1024, 1024, 32, 17), (320, 1792, 64, 5), (5120, 6144, 32, 1), (512, 2048, 192, 100),
-         (96, 768, 12, 2)]
+         (640, 1536, 384, 257), (96, 768, 12, 2)]
 
 
 @pytest.mark.parametrize("n,k,m1,m2", CASES)

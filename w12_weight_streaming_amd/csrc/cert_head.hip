@@ -122,9 +122,8 @@ __global__ __launch_bounds__(256) void cert_pack_kernel(const uint16_t* __restri
   }
 }
 
-// Argmax key layout shared with the GEMM kernels: 8 copies x 256 rows x 16
-// u64 (one 128-byte line per row); copy blockIdx.x % 8.
-constexpr int kKeyCopies = 8, kKeyRows = 256, kKeyStride = 16;
+// Argmax keys in the GEMM kernels' layout (kKeyCopies x kKeyRows x
+// kKeyStride u64, copy blockIdx.x % kKeyCopies).
 constexpr int kGroupsPerWave = 16;
 constexpr int kRecUnroll = 5;  // records a lane has in flight in the rescoring
 

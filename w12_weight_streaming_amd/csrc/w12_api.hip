@@ -125,7 +125,7 @@ CertLayout cert_layout(int64_t n, int64_t k, int64_t m, int cu) {
   L.pl = w12::plan_gemm(n, k, m, cu);
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   L.off_keys2 = 0;
-  L.off_done2 = size_t(8) * 8 * 256 * 16;
+  L.off_done2 = w12::kKeyRegionBytes;
   L.off_list_count = L.off_done2 + 128;  // its own cache line
   L.off_counts = L.off_done2 + 256;
   L.off_xnorm = L.off_counts + 256;

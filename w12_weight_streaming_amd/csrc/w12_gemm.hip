@@ -180,9 +180,8 @@ __device__ __forceinline__ unsigned long long kmax(unsigned long long x, unsigne
 // lines instead of queueing on the two lines 32 packed keys would share. The
 // last workgroup takes the maximum of the 8 copies (max is order-free, so the
 // result does not depend on which XCD ran what).
-constexpr int kKeyCopies = 8;
-constexpr int kKeyRows = 256;    // >= rows per launch
-constexpr int kKeyStride = 16;   // u64 per row: one 128-byte line
+// (kKeyCopies, kKeyRows, kKeyStride: w12_internal.h, shared with the
+// certified head's rescoring)
 static_assert(kKeyRows >= kRowsPerLaunch, "a key row for every row of a launch");
 __device__ __forceinline__ unsigned long long* key_slot(const GemmParams& a, int m) {
   return a.keys + ((int)(blockIdx.x % kKeyCopies) * kKeyRows + m) * kKeyStride;
@@ -1536,7 +1535,7 @@ KernelSel select_kernel(int M, int nq) {
 }  // namespace
 
 constexpr size_t kCounterBytes = size_t(4) << 18;              // u32 per tile, P <= 2^18
-constexpr size_t kKeyBytes = size_t(8) * kKeyCopies * kKeyRows * kKeyStride;  // argmax keys
+constexpr size_t kKeyBytes = kKeyRegionBytes;  // argmax keys
 constexpr size_t kStateBytes = kCounterBytes + kKeyBytes + 256;                 // + done counter
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq) {

@@ -27,11 +27,20 @@ constexpr int kCertCbFloats = 4096;
 // rows of the certified head (one MFMA path, at most two 32-row tiles)
 constexpr int kCertMaxRows = 64;
 
-// Rows up to kSmallMaxRows run the small-m kernels (64-channel tiles); more
-// rows, up to kRowsPerLaunch per launch, the large-m kernel (128-channel
-// tiles). Larger m is split into launches of kRowsPerLaunch rows.
+// Rows up to kSmallMaxRows run the small-m kernels (64- or 128-channel
+// tiles); more rows, up to kRowsPerLaunch per launch, the large-m kernel
+// (128-channel tiles). Larger m is split into launches of kRowsPerLaunch rows.
 constexpr int kSmallMaxRows = 64;
 constexpr int kRowsPerLaunch = 192;
+
+// Argmax keys in a workspace: kKeyCopies copies (workgroup b uses copy
+// b % kKeyCopies, one per XCD) x kKeyRows rows x kKeyStride u64 (one
+// 128-byte line per row). The certified head reads and clears its lower
+// bounds in the same layout.
+constexpr int kKeyCopies = 8;
+constexpr int kKeyRows = 256;  // >= kRowsPerLaunch
+constexpr int kKeyStride = 16;
+constexpr size_t kKeyRegionBytes = size_t(8) * kKeyCopies * kKeyRows * kKeyStride;
 
 // One verify GEMM (or LM head) launch. Work is split stream-K style: a unit
 // is one record of a tile (2 strips of 32 channels for small m, 4 for large
