@@ -573,7 +573,7 @@ def run_sweep(args, w12, synth, torch, dev):
     """Time flatness in rows: Wgate|Wup 34816x5120 (block weight recipe) at
     M = 1 ... 512, over >= 1 GiB of distinct packed copies, bf16 out. Above
     192 rows a call runs as launches of at most 192 rows."""
-    rows = (1, 8, 12, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512)
+    rows = (1, 2, 4, 5, 8, 12, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512)
     w = torch.cat([synth.weights_bf16(FFN, HIDDEN, seed=1_000_000 * 2 + j, device=dev) for j in (5, 6)], dim=0)
     pw = w12.w12_pack(w, check=True)
     del w

@@ -161,8 +161,8 @@ w12_status w12_gemm_workspace(int64_t n, int64_t k, int64_t m, size_t *bytes);
 /*
  * w12_gemm -- verify GEMM ([S1] 4.1): y[i, c] = sum_k x[i, k] * W[c, k] for
  * the m verify rows, streaming every W12 record from HBM once, restoring it
- * in registers, fp32 accumulation. Rows m < 16 use a VALU dot-product path,
- * m >= 16 bf16 MFMA (more than 192 rows run as several launches of at most
+ * in registers, fp32 accumulation. Rows m <= 4 use a VALU dot-product path,
+ * m >= 5 bf16 MFMA (more than 192 rows run as several launches of at most
  * 192 rows, each streaming W again). The reduction over k is split across workgroups in a
  * fixed order (stream-K), so results are bitwise reproducible.
  *   x   [m, k] bf16 row-major, 1 <= m <= 512.
@@ -185,7 +185,7 @@ w12_status w12_gemm(const w12_matrix *w, const uint16_t *x, int64_t m,
  *   Returns W12_ENOSPC, before launching anything, when w12_gemm_workspace
  *   for the shape exceeds W12_NOALLOC_SCRATCH_BYTES. At 256 compute units
  *   every m <= 512 fits for k <= 400000 (192-row launches need 51.6 MB;
- *   16 <= m <= 64 adds 128 * k bytes of x fragments).
+ *   5 <= m <= 64 adds 128 * k bytes of x fragments).
  *   The first call on a device looks up the array's device address and
  *   enqueues one kernel on `stream` that zero-fills it; every completed call
  *   leaves its counters at zero again.

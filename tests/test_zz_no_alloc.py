@@ -69,7 +69,7 @@ def test_noalloc_equals_gemm_on_two_calls(w12, n, k, m1, m2):
 
 def test_noalloc_scratch_fits_the_workloads_and_refuses_beyond(w12):
     """Every shape of the verify pass, the LM head and the batched case fits
-    the scratch; a shape whose workspace does not (16 <= m <= 64 needs 128 k
+    the scratch; a shape whose workspace does not (5 <= m <= 64 needs 128 k
     bytes of x fragments: k = 2^20) is refused with W12_ENOSPC. The refused
     call is made only after the library's own size query has said that the
     shape exceeds the scratch, so it cannot reach a launch."""

@@ -131,7 +131,7 @@ CertLayout cert_layout(int64_t n, int64_t k, int64_t m, int cu) {
   L.off_xnorm = L.off_counts + 256;
   L.off_gemm = L.off_xnorm + 256;
   // the INT8 pass runs the MFMA kernel for every m, so its x fragments need
-  // ceil(m / 32) tiles even below 16 rows (where plan_gemm reserves none)
+  // ceil(m / 32) tiles even below kMfmaMinRows rows (where plan_gemm reserves none)
   const size_t xf_end = L.pl.off_xf + (size_t)((m + 31) / 32) * 32 * (size_t)k * 2;
   L.off_u4 = up(L.off_gemm + (L.pl.ws_bytes > xf_end ? L.pl.ws_bytes : xf_end));
   L.off_list = up(L.off_u4 + (size_t)(n / 4) * w12::kCertMaxRows * 4);

@@ -21,11 +21,12 @@
 //  * Loads run D units ahead of the arithmetic and are always issued
 //    unconditionally; the loop has no barrier that waits on vector memory,
 //    so the next units' loads stay in flight across every barrier.
-//  * 16 <= m <= 64: bf16 MFMA 32x32x16, weights = A, x = B. The B fragments come
-//    from a copy of x rearranged once per call so that every fragment load
-//    is one contiguous 1 KB per wave (xfrag_kernel).
-//  * m < 16: lanes own channels, fdot2 against x rows (up to 2 rows read
-//    from memory by every lane of a half-wave; more rows ride in the load
+//  * 5 <= m <= 64: bf16 MFMA 32x32x16, weights = A, x = B (one or two 32-row
+//    x tiles, rows past m zero). The B fragments come from a copy of x
+//    rearranged once per call so that every fragment load is one contiguous
+//    1 KB per wave (xfrag_kernel).
+//  * m <= 4: lanes own channels, fdot2 against x rows (up to 2 rows read
+//    from memory by every lane of a half-wave; 3-4 rows ride in the load
 //    ring and are broadcast through a per-wave LDS buffer).
 //  * Escapes (~1% of weights here): restored pairs go through a per-wave LDS
 //    buffer, the lanes holding the block's escape entries overwrite their
@@ -743,7 +744,7 @@ __device__ __forceinline__ uint32_t bias2_of_top(uint32_t et4, int lane) {
   return __builtin_amdgcn_ubfe(et4, 8u * (uint32_t)(lane & 3), 8) * 0x00800080u - 0x07800780u;
 }
 
-// ============================================================================ MFMA path (m >= 16)
+// ============================================================================ MFMA path (5 <= m <= 64)
 
 template <int MT, int EPI, bool QP, int NQ, int FMT = kFmtW12>
 __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
@@ -915,7 +916,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   finish_slice<EPI, kNT, TC, 2>(a, tid, u0, u1, &s_last);
 }
 
-// ============================================================================ VALU path (m < 16)
+// ============================================================================ VALU path (m <= 4)
 
 template <int MV, int EPI, bool QP>
 __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
@@ -926,10 +927,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // 1 KB LDS buffer, from which the half-waves read their rows as broadcasts.
   constexpr bool kXLds = MV > 2;
   constexpr int XQ = kXLds ? 1 : MV;
-  // 16 rows of accumulators and a ring two units deep do not fit the register
-  // file (the kernel spilled to scratch and ran 13-15 rows at ~170 us on
-  // Wgate|Wup, twice the time at 12 rows); one unit deep they nearly do.
-  constexpr int kValuDepth = MV > 12 ? 1 : kDepth;
+  constexpr int kValuDepth = kDepth;
   __shared__ __align__(16) float lds[kLdsFloats];
   __shared__ __align__(16) char xlds[kXLds ? kNW * 1024 : 16];
   __shared__ int s_last;
@@ -1514,18 +1512,19 @@ KernelSel select_kernel(int M, int nq) {
         return {nullptr, 0, 0};
     }
   }
-  if (M >= 16) {
+  if (M >= kMfmaMinRows) {
     if (M <= 32)
       return nq == 4 ? KernelSel{reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 4>), 1, kNT}
                      : KernelSel{reinterpret_cast<const void*>(&gemm_mfma_kernel<1, EPI, QP, 2>), 1, kNT};
     return {reinterpret_cast<const void*>(&gemm_mfma_kernel<2, EPI, QP, 2>), 2, kNT};
   }
-  const int mv = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 12 ? 12 : 16;
+  static_assert(kMfmaMinRows <= 5, "the VALU path is instantiated for up to 4 rows");
+  const int mv = M <= 1 ? 1 : M <= 2 ? 2 : 4;
   switch (mv) {
 #define W12_VALU(MV) \
   case MV:           \
     return {reinterpret_cast<const void*>(&gemm_valu_kernel<MV, EPI, QP>), 0, kNT};
-    W12_VALU(1) W12_VALU(2) W12_VALU(4) W12_VALU(8) W12_VALU(12) W12_VALU(16)
+    W12_VALU(1) W12_VALU(2) W12_VALU(4)
 #undef W12_VALU
     default:
       return {nullptr, 0, 0};
@@ -1546,14 +1545,14 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq) {
   // fragment then serves 4 strips, and tiles end half as often); shorter
   // slices keep 2-strip tiles, whose finer units balance the slices better.
   int nq = 2;
-  if (!big && m >= 16 && m <= 32 && max_nq >= 4) {
+  if (!big && m >= kMfmaMinRows && m <= 32 && max_nq >= 4) {
     const int64_t U4 = ((S + 3) / 4) * RK;
     const int64_t G4 = U4 < num_cu ? U4 : num_cu;
     if (U4 >= (int64_t)kNq4MinUnits * G4) nq = 4;
   }
   const int64_t tc = big ? kBigTC : nq * kStrip;  // channels per tile of the kernel select_kernel picks
   const int64_t sp = tc / kStrip, P = (S + sp - 1) / sp;
-  const int64_t mt = (!big && m >= 16) ? (m + 31) / 32 : 0;
+  const int64_t mt = (!big && m >= kMfmaMinRows) ? (m + 31) / 32 : 0;
   const int64_t U = P * RK;
   // one workgroup per compute unit, every slice resident at once
   int64_t G = num_cu;

@@ -32,6 +32,12 @@ constexpr int kCertMaxRows = 64;
 // (128-channel tiles). Larger m is split into launches of kRowsPerLaunch rows.
 constexpr int kSmallMaxRows = 64;
 constexpr int kRowsPerLaunch = 192;
+// Rows from which the small-m path multiplies on the matrix cores (one
+// 32-row x tile, rows past m zero); fewer rows take the VALU dot products.
+// Measured on Wgate|Wup 34816x5120: 57 us for every m in 5..16 on the
+// matrix cores, against 67-98 us on the VALU path; 1-4 rows are level
+// (53-59 us) and stay on the VALU path, which is 2 us faster on Wo.
+constexpr int kMfmaMinRows = 5;
 
 // Argmax keys in a workspace: kKeyCopies copies (workgroup b uses copy
 // b % kKeyCopies, one per XCD) x kKeyRows rows x kKeyStride u64 (one
@@ -57,7 +63,7 @@ struct GemmParams {
   int nq;  // strips per tile of the small-m MFMA kernel (from the plan)
   void* y;
   int ytype;
-  uint4* xf;              // x rearranged into MFMA B fragments (m >= 16)
+  uint4* xf;              // x rearranged into MFMA B fragments (m >= kMfmaMinRows)
   float* part;            // [2G][M][tile channels] split-tile partial sums
   uint32_t* tile_cnt;     // [P] arrival counters, zero between calls
   unsigned long long* keys;  // argmax keys: 8 copies x 256 rows x 16 u64 (one line per row), zero between calls
