@@ -48,9 +48,9 @@ LAYER_SHAPES = (("QKV", Q_OUT + 2 * KV_OUT, HIDDEN), ("O", HIDDEN, Q_OUT),
                 ("UP", 2 * FFN, HIDDEN), ("DOWN", HIDDEN, FFN))
 # kernel each call type runs at M=32 (the plan picks 2-strip tiles for the
 # block shapes and 4-strip tiles for the head)
-KERNEL_OF = {"QKV": "gemm_mfma_kernel<1, 0, false, 2>", "O": "gemm_mfma_kernel<1, 0, false, 2>",
-             "UP": "gemm_mfma_kernel<1, 0, false, 2>", "DOWN": "gemm_mfma_kernel<1, 0, false, 2>",
-             "HEAD": "gemm_mfma_kernel<1, 1, false, 4>", "TREE": "tree_accept_kernel"}
+KERNEL_OF = {"QKV": "gemm_mfma_kernel<1, 0, false, 2, 0>", "O": "gemm_mfma_kernel<1, 0, false, 2, 0>",
+             "UP": "gemm_mfma_kernel<1, 0, false, 2, 0>", "DOWN": "gemm_mfma_kernel<1, 0, false, 2, 0>",
+             "HEAD": "gemm_mfma_kernel<1, 1, false, 4, 0>", "TREE": "tree_accept_kernel"}
 
 
 def log(*a):
