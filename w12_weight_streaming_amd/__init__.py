@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libw12.so")
 
 W12_OK, W12_EINVAL, W12_ENOSPC, W12_EHIP, W12_ECORRUPT = 0, -1, -2, -3, -4
 W12_Y_F32, W12_Y_BF16 = 0, 1
-MFMA_MIN_ROWS = 16
+MFMA_MIN_ROWS = 5  # rows from which w12_gemm multiplies on the matrix cores (fewer: VALU path)
 MAX_ROWS = 512
 
 _lib = None
