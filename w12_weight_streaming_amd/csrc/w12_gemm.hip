@@ -767,7 +767,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = logical_wg(blockIdx.x, a.G);
-  const int U = a.U, RK = a.RK, S = a.S;
+  const int U = a.U, RK = a.RK;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
   char* patch = reinterpret_cast<char*>(lds) + wave * (NQ * 2048);
   static_assert(kNW * NQ * 2048 <= kNW * SF * 4, "patch buffers fit in the reduction slots");
@@ -935,7 +935,7 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = logical_wg(blockIdx.x, a.G);
-  const int U = a.U, RK = a.RK, S = a.S;
+  const int U = a.U, RK = a.RK;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
   char* patch = reinterpret_cast<char*>(lds) + wave * 4096;
 
@@ -1253,7 +1253,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sw = wave & 3, kg = wave >> 2;
   const int g = logical_wg(blockIdx.x, a.G);
-  const int U = a.U, RK = a.RK, S = a.S;
+  const int U = a.U, RK = a.RK;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
   char* patch = lds + 2 * Lds::kX + wave * 4096;
   float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
