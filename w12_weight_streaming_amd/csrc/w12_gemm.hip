@@ -1253,7 +1253,7 @@ __global__ __launch_bounds__(kB8NT) void gemm_big8_kernel(GemmParams a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sw = wave & 3, kg = wave >> 2;
   const int g = logical_wg(blockIdx.x, a.G);
-  const int U = a.U, RK = a.RK;
+  const int U = a.U, RK = a.RK, S = a.S;
   const int u0 = chunk_begin(g, U, a.G), u1 = chunk_begin(g + 1, U, a.G);
   char* patch = lds + 2 * Lds::kX + wave * 4096;
   float* red = reinterpret_cast<float*>(lds + 2 * Lds::kX + Lds::kPatch);
