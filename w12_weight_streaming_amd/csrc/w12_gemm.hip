@@ -817,6 +817,19 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   // ---- tile end: reduce the 8 waves' accumulators, write or hand off. Every
   // wave writes its 32 x 64 partial to a slot of its own, then each thread
   // sums one row quad over the 8 slots in a fixed order.
+  // The partial of a split tile that ends inside the slice (only the first
+  // tile can) is stored after the walk, not when the tile ends: a store
+  // issued between record loads holds back the completion count of every
+  // later load until it is acknowledged, and a write-through store at device
+  // scope is acknowledged slowly under the record stream (measured: 3.5 us per
+  // Wgate|Wup launch at 32 rows, 9 us on the LM head). Until then each thread
+  // keeps its own quads in LDS, or in registers for the INT8 pass's 4-strip
+  // tiles, whose LDS is full.
+  constexpr bool kStageInRegs = FMT == kFmtCert8 && NQ == 4;
+  constexpr int kStageQ = MT * (NQ / 2);  // float4 per thread
+  __shared__ __align__(16) float4 stage[kStageInRegs ? 1 : kStageQ * kNT];
+  float4 stage_r[kStageInRegs ? kStageQ : 1];
+  const int p_last = (u1 - 1) / RK;
   auto flush = [&](int p) __attribute__((always_inline)) {
     const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
@@ -856,8 +869,12 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
           } else {
             emit4<EPI>(a, tid, m, p * TC + c4, v);
           }
-        } else if (m < a.M) {
-          store_partial<TC>(a, slot, m, c4, v);
+        } else if (p == p_last) {
+          if (m < a.M) store_partial<TC>(a, slot, m, c4, v);
+        } else if constexpr (kStageInRegs) {
+          stage_r[mt * (NQ / 2) + h] = v;
+        } else {
+          stage[(mt * (NQ / 2) + h) * kNT + tid] = v;
         }
       }
     });
@@ -906,6 +923,17 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
   if (u0 < u1) {
     walk_slice<XQ, NQ, D>(L, u0, u1, issue_x, step);
+    if (const int p0 = u0 / RK; p0 != p_last && tile_is_split(p0, u0, u1, RK)) {
+      const int slot0 = partial_slot(g, p0, U, a.G, RK);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < NQ / 2; ++h) {
+          const int m = mt * 32 + (tid >> 4), c4 = h * 64 + (tid & 15) * 4;
+          const float4 v = kStageInRegs ? stage_r[mt * (NQ / 2) + h] : stage[(mt * (NQ / 2) + h) * kNT + tid];
+          if (m < a.M) store_partial<TC>(a, slot0, m, c4, v);
+        }
+    }
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax || EPI == kEpiCert) {
