@@ -998,7 +998,12 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     }
   };
 
-  // ---- tile end: fold the two k halves, reduce the 8 waves, write or hand off
+  // ---- tile end: fold the two k halves, reduce the 8 waves, write or hand off.
+  // As in the matrix-core path, a split tile that ends inside the slice has
+  // its partial stored after the walk (held in a register until then).
+  const int p_last = (u1 - 1) / RK;
+  float4 stage = make_float4(0.f, 0.f, 0.f, 0.f);
+  static_assert(MV * 16 <= kNT, "one row quad per thread at a tile end");
   auto flush = [&](int p) __attribute__((always_inline)) {
     const bool whole = !tile_is_split(p, u0, u1, RK);
     const int slot = partial_slot(g, p, U, a.G, RK);
@@ -1023,6 +1028,8 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
         } else {
           emit4<EPI>(a, tid, m, p * 64 + c4, v);
         }
+      } else if (p != p_last) {
+        stage = v;  // at most one quad per thread: MV * 16 <= the workgroup's threads
       } else if (m < a.M) {
         store_partial<64>(a, slot, m, c4, v);
       }
@@ -1078,6 +1085,8 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
 
   if (u0 < u1) {
     walk_slice<XQ, 2, kValuDepth>(L, u0, u1, issue_x, step);
+    if (const int p0 = u0 / RK; p0 != p_last && tile_is_split(p0, u0, u1, RK) && tid < MV * 16 && (tid >> 4) < a.M)
+      store_partial<64>(a, partial_slot(g, p0, U, a.G, RK), tid >> 4, (tid & 15) * 4, stage);
     flush(cur.p);
   }
   if constexpr (EPI == kEpiArgmax) {
