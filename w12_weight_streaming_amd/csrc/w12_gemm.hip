@@ -948,16 +948,16 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 
 template <int MV, int EPI, bool QP>
 __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
-  // x of the wave's subtile rides in the load ring. Up to 2 rows, each lane
-  // carries the 32 bytes of every row it multiplies (lanes of a half-wave
-  // hold the same bytes). For more rows, the wave's block of x (MV rows x 64
-  // bytes) rides as one 16-byte piece per lane and goes through a private
-  // 1 KB LDS buffer, from which the half-waves read their rows as broadcasts.
-  constexpr bool kXLds = MV > 2;
-  constexpr int XQ = kXLds ? 1 : MV;
+  // x of the wave's subtile rides in the load ring: the wave's block of x (up
+  // to 16 rows x 64 bytes) as one 16-byte piece per lane, through a private
+  // 1 KB LDS buffer from which the half-waves read their rows as broadcasts.
+  // (Measured against each lane loading the 32 bytes of every row itself:
+  // Wgate|Wup 34816x5120 52.8 -> 50.8 us at 1 row, 57.7 -> 51.1 us at 2; the
+  // 152064x5120 head 205 -> 194 and 227 -> 195 us; bit-identical.)
+  constexpr int XQ = 1;
   constexpr int kValuDepth = kDepth;
   __shared__ __align__(16) float lds[kLdsFloats];
-  __shared__ __align__(16) char xlds[kXLds ? kNW * 1024 : 16];
+  __shared__ __align__(16) char xlds[kNW * 1024];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -977,26 +977,13 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
   // x rows >= M read 0 (voffset past the range); a record's x starts 512 bytes on.
   UnitLoads<XQ, QP, 2> L(a, wave, lane, u0, u1, a.x, (uint32_t)a.M * (uint32_t)a.K * 2u, 0u, 512u);
   const uint32_t plo = patch_lane_off(lane);
-  // x of this lane: row m, k = 256 r + 32 wave + 16 (lane / 32) .. +15
-  const uint32_t v_x = (uint32_t)(wave * kSubK + 16 * (lane >> 5)) * 2u;
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
 
   // block piece of this lane: row lane / 4, bytes 16 (lane % 4) of the
   // subtile's 64 (rows >= m read 0)
   const uint32_t v_xp = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)(wave * kSubK) * 2u + (uint32_t)(lane & 3) * 16u;
-  char* xw = xlds + (kXLds ? wave * 1024 : 0);
-  auto issue_x = [&](Slot<XQ, 2>& s) __attribute__((always_inline)) {
-    if constexpr (kXLds) {
-      s.xv[0][0] = bload4(L.rx, v_xp, L.sx);
-    } else {
-#pragma unroll
-      for (int m = 0; m < XQ; ++m) {
-        const uint32_t vx = v_x + m * row_bytes;
-        s.xv[m][0] = bload4(L.rx, vx, L.sx);
-        s.xv[m][1] = bload4(L.rx, vx + 16, L.sx);
-      }
-    }
-  };
+  char* xw = xlds + wave * 1024;
+  auto issue_x = [&](Slot<XQ, 2>& s) __attribute__((always_inline)) { s.xv[0][0] = bload4(L.rx, v_xp, L.sx); };
 
   // ---- tile end: fold the two k halves, reduce the 8 waves, write or hand off.
   // As in the matrix-core path, a split tile that ends inside the slice has
@@ -1062,24 +1049,16 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     const uint32_t bias[2] = {bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane)};
     uint32_t P[2][8];
     restore_unit<2>(s, bias, patch, plo, lane, L.r_esc, P);
-    if constexpr (kXLds) {
-      wave_lds_order();  // the previous unit's reads of the buffer come first
-      *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
-      wave_lds_order();
-      const char* xr = xw + 32 * (lane >> 5);
+    wave_lds_order();  // the previous unit's reads of the buffer come first
+    *reinterpret_cast<u32x4*>(xw + lane * 16) = s.xv[0][0];
+    wave_lds_order();
+    const char* xr = xw + 32 * (lane >> 5);
 #pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(xr + m * 64);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(xr + m * 64 + 16);
-        acc[0][m] = dot16(P[0], x0, x1, acc[0][m]);
-        acc[1][m] = dot16(P[1], x0, x1, acc[1][m]);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        acc[0][m] = dot16(P[0], s.xv[m][0], s.xv[m][1], acc[0][m]);
-        acc[1][m] = dot16(P[1], s.xv[m][0], s.xv[m][1], acc[1][m]);
-      }
+    for (int m = 0; m < MV; ++m) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(xr + m * 64);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(xr + m * 64 + 16);
+      acc[0][m] = dot16(P[0], x0, x1, acc[0][m]);
+      acc[1][m] = dot16(P[1], x0, x1, acc[1][m]);
     }
   };
 
