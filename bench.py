@@ -622,8 +622,8 @@ def run_qpass(args, w12, synth, torch, dev):
     head_pw, head_x, _, _ = pack_head(w12, synth, torch, dev)
     order = ["QKV", "O", "UP", "DOWN"]
     outs = {n: torch.empty(M_ROWS, mats[n][0].n, dtype=torch.bfloat16, device=dev) for n in order}
-    ws = w12.workspace(max(w12.gemm_workspace_bytes(mats[n][0].n, mats[n][0].k, M_ROWS)
-                           for n in order + ["HEAD"]), dev)
+    ws = w12.workspace(max([w12.gemm_workspace_bytes(mats[n][0].n, mats[n][0].k, M_ROWS) for n in order] +
+                           [w12.gemm_workspace_bytes(head_pw.n, head_pw.k, M_ROWS)]), dev)
 
     def step(qp):
         for n in order:
