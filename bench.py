@@ -588,7 +588,7 @@ def run_sweep(args, w12, synth, torch, dev):
         for i in range(max(args.warmup, ncopy)):
             call(i)
         torch.cuda.synchronize()
-        us = min(time_events(call, max(8, args.steps)) for _ in range(3))
+        us = min(time_events(call, max(32, args.steps)) for _ in range(5))
         nbytes = gemm_bytes(pw, m, 2)
         by_rows[m] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "TFLOPs": round(2.0 * m * pw.n * pw.k / (us * 1e-6) / 1e12, 1)}
@@ -596,7 +596,7 @@ def run_sweep(args, w12, synth, torch, dev):
     v = by_rows[M_ROWS]["GBps"]
     line = {
         "metric": "W12 verify GEMM effective HBM GB/s vs rows (Wgate|Wup 34816x5120)",
-        "value": v, "unit": "GB/s", "n_gpus": 1, "steps": max(8, args.steps), "warmup": args.warmup,
+        "value": v, "unit": "GB/s", "n_gpus": 1, "steps": max(32, args.steps), "warmup": args.warmup,
         "ms_per_step": round(by_rows[M_ROWS]["us"] / 1000.0, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Wgate|Wup 34816x5120 (1.07% escapes), bf16 out, >= 1 GiB of rotated copies; "
