@@ -179,6 +179,40 @@ def test_gemm_within_tolerance(w12, gemm_mats, shape, m):
     assert torch.equal(yb.cpu(), y.cpu().to(torch.bfloat16))
 
 
+@pytest.fixture(scope="module")
+def wide_mat(w12):
+    n, k = 32800, 512
+    bits = synth.bits_u16(gen(n, k, 4321, p_zero=0.03, p_outlier=0.02))
+    pw, _ = pack_gpu(w12, bits)
+    return pw, bits
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 32, 40])
+def test_gemm_slices_spanning_tiles(w12, wide_mat, m):
+    """32800 x 512 (1025 strips, 2 records each): on a 256-CU device the
+    slices hold ~4 units, so most start inside a tile (a split first tile whose
+    partial is kept until the walk ends), cross a whole tile and end inside a
+    third. Every output against the oracle, the GEMM and head argmax each
+    repeated bit for bit on one workspace."""
+    pw, bits = wide_mat
+    say("slices spanning tiles m", m)
+    x = synth.activations_bf16(m, 512, 4400 + m)
+    xd = x.to(DEV)
+    ws = torch.zeros(w12.gemm_workspace_bytes(pw.n, pw.k, m), dtype=torch.uint8, device=DEV)
+    y = w12.w12_gemm(pw, xd, ws=ws).clone()
+    y_ref, bound = V.gemm_ref(synth.bits_u16(x), bits)
+    ok = V.within_tolerance(host(y), y_ref, bound)
+    assert ok.all(), f"{(~ok).sum()} outputs out of tolerance"
+    for _ in range(3):
+        assert torch.equal(w12.w12_gemm(pw, xd, ws=ws), y)
+    idx, mx = w12.w12_head_argmax(pw, xd, ws=ws)
+    ref_idx, _, cands = V.head_argmax(synth.bits_u16(x), bits)
+    check_argmax(host(idx), ref_idx, cands)
+    assert np.array_equal(host(mx), host(y)[np.arange(m), host(idx)])
+    i2, m2 = w12.w12_head_argmax(pw, xd, ws=ws)
+    assert torch.equal(i2, idx) and torch.equal(m2, mx)
+
+
 @pytest.mark.parametrize("m", [1, 8, 32, 64])
 def test_gemm_exact_pins(w12, m):
     """One-hot rows give weight columns exactly; small integers are exact."""
