@@ -1512,7 +1512,8 @@ struct KernelSel {
 
 // Units per slice (at 4 strips per tile) from which m <= 32 uses 4-strip
 // tiles. Measured at 32 rows: the 152064x5120 LM head (93 units per slice)
-// 3% faster with 4 strips, Wgate|Wup 34816x5120 (21) 5% slower.
+// 3% faster with 4 strips; Wgate|Wup 34816x5120 (21) level (59.0 against
+// 59.5 us), since a 4-strip tile keeps one unit of loads in flight, not two.
 constexpr int kNq4MinUnits = 48;
 
 template <int EPI, bool QP>

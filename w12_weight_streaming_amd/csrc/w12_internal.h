@@ -34,9 +34,9 @@ constexpr int kSmallMaxRows = 64;
 constexpr int kRowsPerLaunch = 192;
 // Rows from which the small-m path multiplies on the matrix cores (one
 // 32-row x tile, rows past m zero); fewer rows take the VALU dot products.
-// Measured on Wgate|Wup 34816x5120: 57 us for every m in 5..16 on the
-// matrix cores, against 67-98 us on the VALU path; 1-4 rows are level
-// (53-59 us) and stay on the VALU path, which is 2 us faster on Wo.
+// Measured on Wgate|Wup 34816x5120: 56.5-56.8 us for every m in 5..16 on
+// the matrix cores (x pre-pass included), against 67-98 us on the VALU path;
+// 1-4 rows stay on the VALU path, which takes 52-56 us there.
 constexpr int kMfmaMinRows = 5;
 
 // Argmax keys in a workspace: kKeyCopies copies (workgroup b uses copy
