@@ -4,7 +4,7 @@
 // "SpecPilot ..." summary, section 4.1 (LM-head paragraph): the head keeps
 // an INT8 copy; a per-row Cauchy-Schwarz error bound proves which tokens
 // cannot be the argmax; only the survivors are rescored exactly, so the
-// argmax never changes. Readings for this build:
+// argmax never changes. Readings taken where the pages leave it open:
 //  * copy: per vocabulary row and 32-k block, the weights W12 keeps in its
 //    window become q = RNE(w / 2^s), s the smallest integer with every such
 //    |w| <= 127 * 2^s (q * 2^s is exact in bf16); W12's escapes are q = 0
