@@ -526,7 +526,8 @@ struct Slot {
   u32x2 off[NQ];       // per strip: esc_off of the escape block and of the next one (every lane)
   u32x4 hi[NQ];        // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[NQ];        // their low nibbles
-  uint32_t et[NQ];     // the 4 window tops around the lane's channel (its byte: lane % 4)
+  uint32_t et[NQ];     // W12: et[0] = dword lane % (8 NQ) of the tile's window tops; INT8 copy:
+                       // per strip, the 4 block scale codes around the lane's channel (byte lane % 4)
   uint32_t e[NQ];      // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ][2];     // x operands that ride with the unit
 };
@@ -578,7 +579,7 @@ struct UnitLoads {
   static constexpr uint32_t kStep = kCert ? (uint32_t)kCertRecBytes : (uint32_t)kRecBytes;
   const GemmParams& a;
   int wave, RK, S, u1;
-  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4, sb_strip;
+  uint32_t strip_bytes, v_hi, v_lo, v_l4, v_c4, v_et, sb_strip;
   rsrc_t r_esc, r_off, r_et;
   const void* x_base;
   uint32_t x_bytes, x_tile, x_step;
@@ -600,6 +601,7 @@ struct UnitLoads {
     v_lo = (uint32_t)(kHiBytes + wave * 512 + lane * 8);
     v_l4 = (uint32_t)lane * 4u;
     v_c4 = (uint32_t)(lane & 28);
+    v_et = (uint32_t)(lane & (8 * NQ - 1)) * 4u;
     // escape count = esc_off[nb]; entries past it read as zero
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
@@ -683,7 +685,15 @@ struct UnitLoads {
       }
       // a whole dword: a byte load's result would be widened where the ring
       // wraps round, which makes the compiler wait for the load right there
-      s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * sb_strip);
+      if constexpr (kCert) {
+        s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * sb_strip);
+      } else if (q == 0) {
+        // the tile's window tops, one load for all NQ strips: lane l holds
+        // dword l % (8 NQ); each lane fetches its strips' dwords with a lane
+        // permute at the unit's arithmetic (LM head, 4-strip tiles: 207.7 ->
+        // 199.8 us against a load per strip)
+        s.et[0] = bload1(r_et, v_et, sb);
+      }
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
@@ -903,7 +913,7 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
       if constexpr (FMT == kFmtCert8) {
         bias[q] = __builtin_amdgcn_ubfe(s.et[q], 8u * (uint32_t)(lane & 3), 8);  // block scale code
       } else {
-        bias[q] = bias2_of_top(s.et[q], lane);
+        bias[q] = bias2_of_top((uint32_t)__builtin_amdgcn_ds_bpermute((q * 8 + ((lane & 31) >> 2)) * 4, (int)s.et[0]), lane);
       }
     }
     uint32_t P[NQ][8];
@@ -1046,7 +1056,8 @@ __global__ __launch_bounds__(kNT) void gemm_valu_kernel(GemmParams a) {
     }
     --cur.left;
     ++cur.u;
-    const uint32_t bias[2] = {bias2_of_top(s.et[0], lane), bias2_of_top(s.et[1], lane)};
+    const uint32_t bias[2] = {bias2_of_top((uint32_t)__builtin_amdgcn_ds_bpermute(((lane & 31) >> 2) * 4, (int)s.et[0]), lane),
+                              bias2_of_top((uint32_t)__builtin_amdgcn_ds_bpermute((8 + ((lane & 31) >> 2)) * 4, (int)s.et[0]), lane)};
     uint32_t P[2][8];
     restore_unit<2>(s, bias, patch, plo, lane, L.r_esc, P);
     wave_lds_order();  // the previous unit's reads of the buffer come first
