@@ -467,7 +467,8 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
     // a block holds at most 1024 weights: corrupt offsets cannot make the
     // patch loop run longer (entries are read through a resource that ends
     // at the escape count, so reads stay in bounds either way)
-    cq[q] = min(max(__builtin_amdgcn_readfirstlane((int)(s.off[q].y - s.off[q].x)), 0), 1024);
+    const u32x2 oq = s.off_of(q);
+    cq[q] = min(max((int)(oq.y - oq.x), 0), 1024);
     any |= cq[q];
   }
 #pragma unroll
@@ -486,7 +487,7 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
     for (int q = 0; q < NQ; ++q) {
       if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
       if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
-        const uint32_t o = __builtin_amdgcn_readfirstlane(s.off[q].x);
+        const uint32_t o = s.off_of(q).x;
         for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
       }
     }
@@ -523,7 +524,10 @@ struct StreamPos {
 // One unit's loads for one wave (subtile t = wave of each of the NQ strips of a tile).
 template <int XQ, int NQ>
 struct Slot {
-  u32x2 off[NQ];       // per strip: esc_off of the escape block and of the next one (every lane)
+  u32x2 off[NQ];       // off[0], lane q < NQ: esc_off of strip q's escape block and of the next one
+  __device__ __forceinline__ u32x2 off_of(int q) const {
+    return u32x2{(uint32_t)__builtin_amdgcn_readlane((int)off[0].x, q), (uint32_t)__builtin_amdgcn_readlane((int)off[0].y, q)};
+  }
   u32x4 hi[NQ];        // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[NQ];        // their low nibbles
   uint32_t et[NQ];     // W12: et[0] = dword lane % (8 NQ) of the tile's window tops; INT8 copy:
@@ -561,9 +565,10 @@ constexpr uint32_t kMidNibbles = 0x88888888u;
 //    tile's strips that exist, so a missing strip (the strip count is not a
 //    multiple of NQ) reads zeros; past the slice the resources are empty and
 //    the loads move no data. A missing strip's channels are never stored.
-//  * O stream (escape-block offsets, read by every lane through a resource
-//    that covers esc_off exactly). A missing strip, or a tile past the last,
-//    reads 1 GiB further on, out of range: offsets 0, 0, no escapes.
+//  * O stream (escape-block offsets, one load per unit: lane q % NQ reads the
+//    pair of strip q % NQ through a resource that covers esc_off exactly). A
+//    missing strip, or a tile past the last, reads 1 GiB further on, out of
+//    range: offsets 0, 0, no escapes.
 //  * E (escape entries): lane l reads entry o0 + l through a resource that
 //    covers the n_esc entries; lanes past the block's count are not used.
 constexpr uint32_t kOutOfRange = 1u << 30;
@@ -589,7 +594,8 @@ struct UnitLoads {
   uint32_t so, sx, sb;
   // O stream
   StreamPos o;
-  uint32_t oo, om[NQ];
+  uint32_t oo, v_om;
+  int lane_q;
 
   __device__ __forceinline__ UnitLoads(const GemmParams& a_, int wave_, int lane, int u0, int u1_,
                                        const void* xb, uint32_t xbytes, uint32_t xtile, uint32_t xstep)
@@ -602,6 +608,7 @@ struct UnitLoads {
     v_l4 = (uint32_t)lane * 4u;
     v_c4 = (uint32_t)(lane & 28);
     v_et = (uint32_t)(lane & (8 * NQ - 1)) * 4u;
+    lane_q = lane % NQ;
     // escape count = esc_off[nb]; entries past it read as zero
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
@@ -655,8 +662,7 @@ struct UnitLoads {
   // The O stream enters tile o.p at record r: escape block (strip, r, wave).
   __device__ __forceinline__ void o_tile(int r) {
     const int sq = NQ * o.p;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) om[q] = (uint32_t)(q * RK) * 32u + (sq + q < S ? 0u : kOutOfRange);
+    v_om = (uint32_t)(lane_q * RK) * 32u + (sq + lane_q < S ? 0u : kOutOfRange);
     oo = (uint32_t)((((sq < S ? sq : 0) * RK + r) * 8 + wave) * 4);
   }
   __device__ __forceinline__ void o_next() {
@@ -670,8 +676,9 @@ struct UnitLoads {
   }
 
   __device__ __forceinline__ void issue_off(Slot<XQ, NQ>& s) const {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) s.off[q] = bload2(r_off, 0u, oo + om[q]);
+    // one load for all strips: lane q (< NQ) reads strip q's pair (the other
+    // lanes repeat it); the strips' pairs come back by readlane
+    s.off[0] = bload2(r_off, v_om, oo);
   }
   __device__ __forceinline__ void issue_w(Slot<XQ, NQ>& s) const {
 #pragma unroll
@@ -698,7 +705,7 @@ struct UnitLoads {
   }
   __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off[q].x * 4u + v_l4, 0);
+    for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off_of(q).x * 4u + v_l4, 0);
   }
 };
 
