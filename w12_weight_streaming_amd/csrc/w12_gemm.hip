@@ -483,12 +483,25 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
 #pragma unroll
     for (int q = 0; q < NQ; ++q) patch_store(patch + q * 2048, plo, P[q]);
     wave_lds_order();
+    if constexpr (NQ == 2) {
+      // one entry load for both strips: lane l holds entry l % 32 of strip l / 32
+      const int ql = lane >> 5;
+      if ((lane & 31) < (ql ? cq[1] : cq[0])) patch_put(patch + ql * 2048, s.e[0]);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
-      if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
-        const uint32_t o = s.off_of(q).x;
-        for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
+      for (int q = 0; q < 2; ++q) {
+        if (cq[q] > 32) {  // more than 32 entries: rare, read the rest here
+          const uint32_t o = s.off_of(q).x;
+          for (int j = 32 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (lane < cq[q]) patch_put(patch + q * 2048, s.e[q]);
+        if (cq[q] > 64) {  // more than one entry per lane: rare, read the rest here
+          const uint32_t o = s.off_of(q).x;
+          for (int j = 64 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
+        }
       }
     }
     wave_lds_order();
@@ -569,8 +582,10 @@ constexpr uint32_t kMidNibbles = 0x88888888u;
 //    pair of strip q % NQ through a resource that covers esc_off exactly). A
 //    missing strip, or a tile past the last, reads 1 GiB further on, out of
 //    range: offsets 0, 0, no escapes.
-//  * E (escape entries): lane l reads entry o0 + l through a resource that
-//    covers the n_esc entries; lanes past the block's count are not used.
+//  * E (escape entries): lane l reads entry o0 + l of each strip's block
+//    (2-strip tiles: one load, entry l % 32 of strip l / 32) through a
+//    resource that covers the n_esc entries; lanes past the block's count
+//    are not used.
 constexpr uint32_t kOutOfRange = 1u << 30;
 
 // FMT = kFmtCert8 streams the certified head's INT8 copy instead: 8 KB
@@ -596,6 +611,7 @@ struct UnitLoads {
   StreamPos o;
   uint32_t oo, v_om;
   int lane_q;
+  bool lane_q2;
 
   __device__ __forceinline__ UnitLoads(const GemmParams& a_, int wave_, int lane, int u0, int u1_,
                                        const void* xb, uint32_t xbytes, uint32_t xtile, uint32_t xstep)
@@ -609,6 +625,7 @@ struct UnitLoads {
     v_c4 = (uint32_t)(lane & 28);
     v_et = (uint32_t)(lane & (8 * NQ - 1)) * 4u;
     lane_q = lane % NQ;
+    lane_q2 = lane >= 32;
     // escape count = esc_off[nb]; entries past it read as zero
     const uint32_t n_esc = scalar_view(a.w.esc_off)[a.w.nb];
     r_esc = make_rsrc(a.w.esc, n_esc < (1u << 30) ? n_esc * 4u : 0xFFFFFFFCu);
@@ -704,8 +721,15 @@ struct UnitLoads {
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
+    if constexpr (NQ == 2) {
+      // one load for both strips: lane l reads entry l % 32 of strip l / 32
+      // (a block with more than 32 entries reads the rest at its patch)
+      const uint32_t o0 = s.off_of(0).x, o1 = s.off_of(1).x;
+      s.e[0] = bload1(r_esc, (lane_q2 ? o1 : o0) * 4u + (v_l4 & 124u), 0);
+    } else {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off_of(q).x * 4u + v_l4, 0);
+      for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off_of(q).x * 4u + v_l4, 0);
+    }
   }
 };
 
