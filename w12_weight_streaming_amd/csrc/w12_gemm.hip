@@ -483,12 +483,15 @@ __device__ __forceinline__ void restore_unit(const SlotT& s, const uint32_t (&bi
 #pragma unroll
     for (int q = 0; q < NQ; ++q) patch_store(patch + q * 2048, plo, P[q]);
     wave_lds_order();
-    if constexpr (NQ == 2) {
-      // one entry load for both strips: lane l holds entry l % 32 of strip l / 32
+    if constexpr (NQ % 2 == 0) {
+      // one entry load per pair of strips: lane l holds entry l % 32 of
+      // strip 2 i + l / 32 in e[i]
       const int ql = lane >> 5;
-      if ((lane & 31) < (ql ? cq[1] : cq[0])) patch_put(patch + ql * 2048, s.e[0]);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int i = 0; i < NQ / 2; ++i)
+        if ((lane & 31) < (ql ? cq[2 * i + 1] : cq[2 * i])) patch_put(patch + (2 * i + ql) * 2048, s.e[i]);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
         if (cq[q] > 32) {  // more than 32 entries: rare, read the rest here
           const uint32_t o = s.off_of(q).x;
           for (int j = 32 + lane; j < cq[q]; j += 64) patch_put(patch + q * 2048, bload1(r_esc, (o + j) * 4u, 0));
@@ -582,8 +585,8 @@ constexpr uint32_t kMidNibbles = 0x88888888u;
 //    pair of strip q % NQ through a resource that covers esc_off exactly). A
 //    missing strip, or a tile past the last, reads 1 GiB further on, out of
 //    range: offsets 0, 0, no escapes.
-//  * E (escape entries): lane l reads entry o0 + l of each strip's block
-//    (2-strip tiles: one load, entry l % 32 of strip l / 32) through a
+//  * E (escape entries): one load per pair of strips, lane l reads entry
+//    l % 32 of strip l / 32 of the pair's blocks, through a
 //    resource that covers the n_esc entries; lanes past the block's count
 //    are not used.
 constexpr uint32_t kOutOfRange = 1u << 30;
@@ -721,11 +724,15 @@ struct UnitLoads {
     }
   }
   __device__ __forceinline__ void issue_e(Slot<XQ, NQ>& s) const {
-    if constexpr (NQ == 2) {
-      // one load for both strips: lane l reads entry l % 32 of strip l / 32
-      // (a block with more than 32 entries reads the rest at its patch)
-      const uint32_t o0 = s.off_of(0).x, o1 = s.off_of(1).x;
-      s.e[0] = bload1(r_esc, (lane_q2 ? o1 : o0) * 4u + (v_l4 & 124u), 0);
+    if constexpr (NQ % 2 == 0) {
+      // one load per pair of strips: lane l reads entry l % 32 of strip
+      // 2 i + l / 32 (a block with more than 32 entries reads the rest at
+      // its patch)
+#pragma unroll
+      for (int i = 0; i < NQ / 2; ++i) {
+        const uint32_t o0 = s.off_of(2 * i).x, o1 = s.off_of(2 * i + 1).x;
+        s.e[i] = bload1(r_esc, (lane_q2 ? o1 : o0) * 4u + (v_l4 & 124u), 0);
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) s.e[q] = bload1(r_esc, s.off_of(q).x * 4u + v_l4, 0);
