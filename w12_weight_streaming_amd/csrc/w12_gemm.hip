@@ -546,8 +546,8 @@ struct Slot {
   }
   u32x4 hi[NQ];        // 8-bit view: 16 weights of channel lane%32, k half lane/32
   u32x2 lo[NQ];        // their low nibbles
-  uint32_t et[NQ];     // W12: et[0] = dword lane % (8 NQ) of the tile's window tops; INT8 copy:
-                       // per strip, the 4 block scale codes around the lane's channel (byte lane % 4)
+  uint32_t et[NQ];     // et[0]: dword lane % 8 of strip (lane / 8) % NQ's window tops (INT8 copy: of
+                       // the record's block scale codes); the lanes' own come by lane permute
   uint32_t e[NQ];      // escape entry number `lane` of the block (if any)
   u32x4 xv[XQ][2];     // x operands that ride with the unit
 };
@@ -626,7 +626,7 @@ struct UnitLoads {
     v_lo = (uint32_t)(kHiBytes + wave * 512 + lane * 8);
     v_l4 = (uint32_t)lane * 4u;
     v_c4 = (uint32_t)(lane & 28);
-    v_et = (uint32_t)(lane & (8 * NQ - 1)) * 4u;
+    v_et = (uint32_t)((lane >> 3) % NQ) * sb_strip + (uint32_t)(lane & 7) * 4u;
     lane_q = lane % NQ;
     lane_q2 = lane >= 32;
     // escape count = esc_off[nb]; entries past it read as zero
@@ -712,13 +712,12 @@ struct UnitLoads {
       }
       // a whole dword: a byte load's result would be widened where the ring
       // wraps round, which makes the compiler wait for the load right there
-      if constexpr (kCert) {
-        s.et[q] = bload1(r_et, v_c4, sb + (uint32_t)q * sb_strip);
-      } else if (q == 0) {
-        // the tile's window tops, one load for all NQ strips: lane l holds
-        // dword l % (8 NQ); each lane fetches its strips' dwords with a lane
-        // permute at the unit's arithmetic (LM head, 4-strip tiles: 207.7 ->
-        // 199.8 us against a load per strip)
+      if (q == 0) {
+        // one load for all NQ strips: lane l holds dword l % 8 of strip
+        // (l / 8) % NQ (the tile's window tops; for the INT8 copy, the
+        // record's block scale codes); each lane fetches its strips' dwords
+        // with a lane permute at the unit's arithmetic (LM head, 4-strip
+        // tiles: 207.7 -> 199.8 us against a load per strip)
         s.et[0] = bload1(r_et, v_et, sb);
       }
     }
@@ -949,7 +948,8 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       if constexpr (FMT == kFmtCert8) {
-        bias[q] = __builtin_amdgcn_ubfe(s.et[q], 8u * (uint32_t)(lane & 3), 8);  // block scale code
+        bias[q] = __builtin_amdgcn_ubfe((uint32_t)__builtin_amdgcn_ds_bpermute((q * 8 + ((lane & 31) >> 2)) * 4, (int)s.et[0]),
+                                        8u * (uint32_t)(lane & 3), 8);  // block scale code
       } else {
         bias[q] = bias2_of_top((uint32_t)__builtin_amdgcn_ds_bpermute((q * 8 + ((lane & 31) >> 2)) * 4, (int)s.et[0]), lane);
       }
