@@ -502,6 +502,48 @@ def test_full_size_block_matrices(w12, name, n, k):
         assert V.within_tolerance(y[:, cols], y_ref, bound).all(), (name, m)
 
 
+@pytest.fixture(scope="module")
+def wgu_mat(w12):
+    """Wgate|Wup 34816x5120: at 5-32 rows on a 256-CU device the plan takes
+    4-strip tiles for it with the y epilogue (the head is the other shape
+    that does)."""
+    n, k = 34816, 5120
+    w = gen(n, k, 34816, device=DEV)
+    return w12.w12_pack(w), w
+
+
+@pytest.mark.parametrize("m", [5, 16, 32])
+def test_full_size_wgate_wup_four_strip_tiles(w12, wgu_mat, m):
+    """Every channel of three 128-channel tiles (the first, one inside, the
+    last) and 64 more against the oracle; repeats bit for bit on one
+    workspace; bf16 output is the fp32 output rounded; the Q pass on two whole
+    strips against the oracle's Q-pass weights."""
+    pw, w = wgu_mat
+    n, k = pw.n, pw.k
+    say("full wgate|wup m", m)
+    x = synth.activations_bf16(m, k, 300 + m, device=DEV)
+    ws = torch.zeros(w12.gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=DEV)
+    y = w12.w12_gemm(pw, x, ws=ws).clone()
+    rng = np.random.default_rng(m)
+    tiles = [0, int(rng.integers(1, n // 128 - 1)), n // 128 - 1]
+    cols = np.unique(np.concatenate([np.arange(128 * t, 128 * t + 128) for t in tiles]
+                                    + [rng.choice(n, 64, replace=False)]))
+    xb = synth.bits_u16(x)
+    wb = synth.bits_u16(w[torch.as_tensor(cols, device=DEV)])
+    y_ref, bound = V.gemm_ref(xb, wb)
+    ok = V.within_tolerance(host(y)[:, cols], y_ref, bound)
+    assert ok.all(), f"{(~ok).sum()} outputs out of tolerance"
+    for _ in range(2):
+        assert torch.equal(w12.w12_gemm(pw, x, ws=ws), y)
+    yb = w12.w12_gemm(pw, x, ws=ws, out_dtype=torch.bfloat16)
+    assert torch.equal(yb.cpu(), y.cpu().to(torch.bfloat16))
+    yq = host(w12.w12_gemm(pw, x, ws=ws, qpass=True))
+    for s in (int(rng.integers(0, n // 32 - 1)), n // 32 - 1):
+        sb = synth.bits_u16(w[32 * s:32 * s + 32])
+        yr, bd = V.gemm_ref(xb, F.qpass_weights(F.pack(sb), 32, k))
+        assert V.within_tolerance(yq[:, 32 * s:32 * s + 32], yr, bd).all(), ("qpass strip", s)
+
+
 @pytest.mark.parametrize("name,n,k,seed", [("Wdown", 5120, 17408, 77), ("Wup", 17408, 5120, 79)])
 def test_full_size_batched_m192(w12, name, n, k, seed):
     """The batched verify shapes at 192 rows with 3% zeros and 2% x64

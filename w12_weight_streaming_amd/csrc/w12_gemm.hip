@@ -1560,10 +1560,13 @@ struct KernelSel {
 };
 
 // Units per slice (at 4 strips per tile) from which m <= 32 uses 4-strip
-// tiles. Measured at 32 rows: the 152064x5120 LM head (93 units per slice)
-// 3% faster with 4 strips; Wgate|Wup 34816x5120 (21) level (59.0 against
-// 59.5 us), since a 4-strip tile keeps one unit of loads in flight, not two.
-constexpr int kNq4MinUnits = 48;
+// tiles. Measured at 32 rows, per call with the x pre-pass, against 2-strip
+// tiles: the 152064x5120 LM head (93 units per slice) 3% faster; Wgate|Wup
+// 34816x5120 (21 units) 56.1-57.8 against 58.1-61.1 us; Wdown 5120x17408
+// (10.6) 38.2 against 37.5 us and Wo 5120x6144 (3.75) 23.7 against 21.1 us
+// slower: their slices are shorter than a tile, so fewer, coarser units
+// balance worse.
+constexpr int kNq4MinUnits = 16;
 
 template <int EPI, bool QP>
 KernelSel select_kernel(int M, int nq) {
