@@ -94,6 +94,7 @@ w12_status run_gemm(const w12_matrix* w, const uint16_t* x, int64_t m, void* y, 
     p.U = pl.U;
     p.G = pl.G;
     p.nq = pl.nq;
+    p.xdirect = pl.xdirect;
     p.y = y ? static_cast<void*>(static_cast<char*>(y) + m0 * y_row) : nullptr;
     p.ytype = ytype;
     p.part = reinterpret_cast<float*>(base + pl.off_part);
@@ -348,6 +349,7 @@ w12_status w12_head_argmax_certified(const w12_matrix* head, const w12_cert8* ce
   p.U = L.pl.U;
   p.G = L.pl.G;
   p.nq = L.pl.nq;
+  p.xdirect = L.pl.xdirect;
   char* gbase = base + L.off_gemm;
   p.part = reinterpret_cast<float*>(gbase + L.pl.off_part);
   p.xf = reinterpret_cast<uint4*>(gbase + L.pl.off_xf);

@@ -830,12 +830,22 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[q][mt][i] = 0.f;
 
-  // x fragment (record r, subtile t, tile mt, half h) of the fragment buffer
-  // is at ((r * 8 + t) * MT + mt) * 2048 + h * 1024.
-  UnitLoads<XQ, QP, NQ, FMT> L(a, wave, lane, u0, u1, a.xf, (uint32_t)(MT * 32) * (uint32_t)a.K * 2u,
-                               (uint32_t)(wave * MT * 2048), (uint32_t)(MT * 8 * 2048));
+  // x fragment (record r, subtile t, tile mt, half h): lane l holds x[mt * 32
+  // + l % 32][32 (8 r + t) + 16 (l / 32) + 8 h ..]. From the pre-pass's
+  // fragment buffer it is 16 bytes at ((r * 8 + t) * MT + mt) * 2048 + h * 1024
+  // + 16 l; where the plan skips the pre-pass (slices of a few units, whose
+  // call the separate launch would dominate), the lane reads those 16 bytes
+  // of row-major x itself, and rows >= M lie outside the resource and read as
+  // zero.
+  const bool xd = FMT == kFmtW12 && a.xdirect;
+  const uint32_t row_bytes = 2u * (uint32_t)a.K;
+  UnitLoads<XQ, QP, NQ, FMT> L(a, wave, lane, u0, u1, xd ? static_cast<const void*>(a.x) : static_cast<const void*>(a.xf),
+                               xd ? (uint32_t)a.M * row_bytes : (uint32_t)(MT * 32) * row_bytes,
+                               xd ? (uint32_t)(wave * 64) : (uint32_t)(wave * MT * 2048),
+                               xd ? 512u : (uint32_t)(MT * 8 * 2048));
   const uint32_t plo = patch_lane_off(lane);
-  const uint32_t v_x = (uint32_t)lane * 16u;
+  const uint32_t v_x = xd ? (uint32_t)(lane & 31) * row_bytes + 32u * (uint32_t)(lane >> 5) : (uint32_t)lane * 16u;
+  const uint32_t x_mt = xd ? 32u * row_bytes : 2048u, x_h = xd ? 16u : 1024u;
 
   // INT8 pass: the thread's row norms, and the slice's channel constants in
   // LDS (the host checks that they fit; the first tile end's barrier orders
@@ -856,8 +866,8 @@ __global__ __launch_bounds__(kNT) void gemm_mfma_kernel(GemmParams a) {
   auto issue_x = [&](Slot<XQ, NQ>& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < XQ; ++mt) {
-      s.xv[mt][0] = bload4(L.rx, v_x + (uint32_t)(mt * 2048), L.sx);
-      s.xv[mt][1] = bload4(L.rx, v_x + (uint32_t)(mt * 2048 + 1024), L.sx);
+      s.xv[mt][0] = bload4(L.rx, v_x + (uint32_t)mt * x_mt, L.sx);
+      s.xv[mt][1] = bload4(L.rx, v_x + (uint32_t)mt * x_mt + x_h, L.sx);
     }
   };
 
@@ -1568,6 +1578,16 @@ struct KernelSel {
 // balance worse.
 constexpr int kNq4MinUnits = 16;
 
+// Units per slice below which the one-tile (5-32 row) MFMA kernel reads x
+// row-major instead of from the pre-pass's fragments. Measured per call with
+// the same 32 rows (bit-identical results): Wo 5120x6144 (7.5 units) 20.1-20.4
+// against 21.0-22.8 us; Wq|Wk|Wv 8192x5120 (10 units) 20.2-20.5 against
+// 19.8-20.2, Wdown (21) 37.0 against 36.5, Wgate|Wup (21, 4-strip tiles) 59.4
+// against 56.8 and the LM head 214 against 195 us slower: a row-major load
+// touches 32 rows, so the longer the slice, the more that costs against the
+// pre-pass's separate launch.
+constexpr int kXDirectMaxUnits = 8;
+
 template <int EPI, bool QP>
 KernelSel select_kernel(int M, int nq) {
   if (M > kSmallMaxRows) {
@@ -1631,6 +1651,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq) {
   pl.U = (int)U;
   pl.P = (int)P;
   pl.nq = nq;
+  pl.xdirect = (!big && mt == 1 && U < (int64_t)kXDirectMaxUnits * G) ? 1 : 0;
   // The counter region has the same place and size for every shape (any
   // shape's tile counters, the argmax keys and the done counter), so a
   // workspace shared by calls of different shapes never holds old partial
@@ -1675,7 +1696,7 @@ hipError_t launch_gemm(const GemmParams& p, int epi, bool qpass, hipStream_t s) 
   const KernelSel k = qpass ? (epi == kEpiY ? select_kernel<kEpiY, true>(p.M, p.nq) : select_kernel<kEpiArgmax, true>(p.M, p.nq))
                             : (epi == kEpiY ? select_kernel<kEpiY, false>(p.M, p.nq) : select_kernel<kEpiArgmax, false>(p.M, p.nq));
   if (!k.fn) return hipErrorInvalidValue;
-  if (k.mt > 0) {
+  if (k.mt > 0 && !p.xdirect) {
     const int64_t chunks = (int64_t)(p.K / 32) * k.mt * 128;
     const int blocks = (int)((chunks + 255) / 256);
     hipLaunchKernelGGL(xfrag_kernel, dim3(blocks), dim3(256), 0, s, p.x, p.M, p.K, k.mt, p.xf);

@@ -61,6 +61,7 @@ struct GemmParams {
   int U;   // units = P * RK
   int G;   // workgroups
   int nq;  // strips per tile of the small-m MFMA kernel (from the plan)
+  int xdirect;  // small-m MFMA kernel: x fragments straight from row-major x, no pre-pass (from the plan)
   void* y;
   int ytype;
   uint4* xf;              // x rearranged into MFMA B fragments (m >= kMfmaMinRows)
@@ -105,6 +106,7 @@ hipError_t launch_cert_rescore(const CertRescoreArgs& a, int rescore_grid, hipSt
 struct GemmPlan {
   int G, U, P;
   int nq;  // strips per tile of the small-m MFMA kernel (2 or 4)
+  int xdirect;  // 1: the small-m MFMA kernel reads x row-major and the x pre-pass is skipped
   size_t ws_bytes;
   size_t off_cnt, off_part, off_keys, off_done, off_xf;
 };
