@@ -24,7 +24,9 @@
 //  * 5 <= m <= 64: bf16 MFMA 32x32x16, weights = A, x = B (one or two 32-row
 //    x tiles, rows past m zero). The B fragments come from a copy of x
 //    rearranged once per call so that every fragment load is one contiguous
-//    1 KB per wave (xfrag_kernel).
+//    1 KB per wave (xfrag_kernel); where slices are only a few units long,
+//    the kernel reads them from row-major x instead and the call has no
+//    pre-pass.
 //  * m <= 4: lanes own channels, fdot2 against x rows (up to 2 rows read
 //    from memory by every lane of a half-wave; 3-4 rows ride in the load
 //    ring and are broadcast through a per-wave LDS buffer).
