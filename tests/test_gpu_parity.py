@@ -503,24 +503,29 @@ def test_full_size_block_matrices(w12, name, n, k):
 
 
 @pytest.fixture(scope="module")
-def wgu_mat(w12):
-    """Wgate|Wup 34816x5120: at 5-32 rows on a 256-CU device the plan takes
-    4-strip tiles for it with the y epilogue (the head is the other shape
-    that does)."""
-    n, k = 34816, 5120
-    w = gen(n, k, 34816, device=DEV)
-    return w12.w12_pack(w), w
+def four_strip_mats(w12):
+    """At 5-32 rows on a 256-CU device the plan takes 4-strip tiles with the y
+    epilogue for Wgate|Wup 34816x5120 (long slices, x from the pre-pass) and
+    for Wq|Wk|Wv 8192x5120 (short slices, x read row-major, no pre-pass)."""
+    mats = {}
+
+    def get(n, k):
+        if (n, k) not in mats:
+            w = gen(n, k, n + 3 * k, device=DEV)
+            mats[(n, k)] = (w12.w12_pack(w), w)
+        return mats[(n, k)]
+    return get
 
 
 @pytest.mark.parametrize("m", [5, 16, 32])
-def test_full_size_wgate_wup_four_strip_tiles(w12, wgu_mat, m):
+@pytest.mark.parametrize("n,k", [(34816, 5120), (8192, 5120)])
+def test_full_size_four_strip_tiles(w12, four_strip_mats, n, k, m):
     """Every channel of three 128-channel tiles (the first, one inside, the
     last) and 64 more against the oracle; repeats bit for bit on one
     workspace; bf16 output is the fp32 output rounded; the Q pass on two whole
     strips against the oracle's Q-pass weights."""
-    pw, w = wgu_mat
-    n, k = pw.n, pw.k
-    say("full wgate|wup m", m)
+    pw, w = four_strip_mats(n, k)
+    say("full four-strip", n, k, "m", m)
     x = synth.activations_bf16(m, k, 300 + m, device=DEV)
     ws = torch.zeros(w12.gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=DEV)
     y = w12.w12_gemm(pw, x, ws=ws).clone()

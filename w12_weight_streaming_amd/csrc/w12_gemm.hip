@@ -1590,6 +1590,14 @@ constexpr int kNq4MinUnits = 16;
 // pre-pass's separate launch.
 constexpr int kXDirectMaxUnits = 8;
 
+// Short slices (at least this many units, fewer than kXDirectMaxUnits) also
+// take 4-strip tiles: with x read row-major, each x load then serves four
+// strips. Measured at 32 rows, per call: Wq|Wk|Wv 8192x5120 (5 units at 4
+// strips) 18.6-19.1 us against 19.9-20.2 with 2-strip tiles and the x
+// pre-pass; Wo 5120x6144 (3.75 units) 22.0-22.5 against 20.1-20.8, which
+// stays on 2-strip tiles.
+constexpr int kNq4ShortMinUnits = 4;
+
 template <int EPI, bool QP>
 KernelSel select_kernel(int M, int nq) {
   if (M > kSmallMaxRows) {
@@ -1633,13 +1641,16 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int64_t m, int num_cu, int max_nq) {
   const bool big = m > kSmallMaxRows;
   const int64_t S = n / kStrip, RK = k / kRecK;
   // Up to 32 rows, tiles of 4 strips when the slices stay long (each x
-  // fragment then serves 4 strips, and tiles end half as often); shorter
-  // slices keep 2-strip tiles, whose finer units balance the slices better.
+  // fragment then serves 4 strips, and tiles end half as often) or are short
+  // enough for x to be read row-major; slices in between keep 2-strip tiles,
+  // whose finer units balance the slices better.
   int nq = 2;
   if (!big && m >= kMfmaMinRows && m <= 32 && max_nq >= 4) {
     const int64_t U4 = ((S + 3) / 4) * RK;
     const int64_t G4 = U4 < num_cu ? U4 : num_cu;
-    if (U4 >= (int64_t)kNq4MinUnits * G4) nq = 4;
+    if (U4 >= (int64_t)kNq4MinUnits * G4 ||
+        (U4 >= (int64_t)kNq4ShortMinUnits * G4 && U4 < (int64_t)kXDirectMaxUnits * G4))
+      nq = 4;
   }
   const int64_t tc = big ? kBigTC : nq * kStrip;  // channels per tile of the kernel select_kernel picks
   const int64_t sp = tc / kStrip, P = (S + sp - 1) / sp;
