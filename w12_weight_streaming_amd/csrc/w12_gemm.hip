@@ -1576,26 +1576,28 @@ struct KernelSel {
 // tiles: the 152064x5120 LM head (93 units per slice) 3% faster; Wgate|Wup
 // 34816x5120 (21 units) 56.1-57.8 against 58.1-61.1 us; Wdown 5120x17408
 // (10.6) 38.2 against 37.5 us and Wo 5120x6144 (3.75) 23.7 against 21.1 us
-// slower: their slices are shorter than a tile, so fewer, coarser units
-// balance worse.
+// slower with the pre-pass: their slices are shorter than a tile, so fewer,
+// coarser units balance worse (short slices that read x row-major are the
+// exception below).
 constexpr int kNq4MinUnits = 16;
 
 // Units per slice below which the one-tile (5-32 row) MFMA kernel reads x
-// row-major instead of from the pre-pass's fragments. Measured per call with
-// the same 32 rows (bit-identical results): Wo 5120x6144 (7.5 units) 20.1-20.4
-// against 21.0-22.8 us; Wq|Wk|Wv 8192x5120 (10 units) 20.2-20.5 against
-// 19.8-20.2, Wdown (21) 37.0 against 36.5, Wgate|Wup (21, 4-strip tiles) 59.4
-// against 56.8 and the LM head 214 against 195 us slower: a row-major load
+// row-major instead of from the pre-pass's fragments (a row-major load
 // touches 32 rows, so the longer the slice, the more that costs against the
-// pre-pass's separate launch.
-constexpr int kXDirectMaxUnits = 8;
+// pre-pass's separate launch). Measured per call at 32 rows, bit-identical
+// results, against the pre-pass: Wo 5120x6144 (7.5 units) 20.1-20.4 against
+// 21.0-22.8 us; Wdown 5120x17408 on 4-strip tiles (10.6 units) 36.5 against
+// 37.1 us (means of six trials); slower with longer slices: Wq|Wk|Wv
+// 8192x5120 on 2-strip tiles (10 units) 20.2-20.5 against 19.8-20.2, Wgate|Wup
+// (21 units) 59.4 against 56.8 and the LM head 214 against 195 us.
+constexpr int kXDirectMaxUnits = 12;
 
-// Short slices (at least this many units, fewer than kXDirectMaxUnits) also
-// take 4-strip tiles: with x read row-major, each x load then serves four
-// strips. Measured at 32 rows, per call: Wq|Wk|Wv 8192x5120 (5 units at 4
-// strips) 18.6-19.1 us against 19.9-20.2 with 2-strip tiles and the x
-// pre-pass; Wo 5120x6144 (3.75 units) 22.0-22.5 against 20.1-20.8, which
-// stays on 2-strip tiles.
+// Short slices (at least this many units at 4 strips, fewer than
+// kXDirectMaxUnits) also take 4-strip tiles: with x read row-major, each x
+// load then serves four strips. Measured at 32 rows, per call, against 2-strip
+// tiles: Wq|Wk|Wv 8192x5120 (5 units) 18.6-19.1 us against 19.9-20.2 with the
+// x pre-pass; Wdown (10.6 units) as above; Wo 5120x6144 (3.75 units)
+// 22.0-22.5 against 20.1-20.8, which stays on 2-strip tiles.
 constexpr int kNq4ShortMinUnits = 4;
 
 template <int EPI, bool QP>
