@@ -47,10 +47,9 @@ METRIC = "W12 verify-GEMM effective HBM GB/s at M=32 rows; % of MI355X HBM peak"
 LAYER_SHAPES = (("QKV", Q_OUT + 2 * KV_OUT, HIDDEN), ("O", HIDDEN, Q_OUT),
                 ("UP", 2 * FFN, HIDDEN), ("DOWN", HIDDEN, FFN))
 # kernel each call type runs at M=32 on 256 compute units (the plan picks
-# 4-strip tiles for Wq|Wk|Wv, Wgate|Wup and the head, 2-strip tiles for Wo
-# and Wdown)
+# 2-strip tiles for Wo, 4-strip tiles for the others)
 KERNEL_OF = {"QKV": "gemm_mfma_kernel<1, 0, false, 4, 0>", "O": "gemm_mfma_kernel<1, 0, false, 2, 0>",
-             "UP": "gemm_mfma_kernel<1, 0, false, 4, 0>", "DOWN": "gemm_mfma_kernel<1, 0, false, 2, 0>",
+             "UP": "gemm_mfma_kernel<1, 0, false, 4, 0>", "DOWN": "gemm_mfma_kernel<1, 0, false, 4, 0>",
              "HEAD": "gemm_mfma_kernel<1, 1, false, 4, 0>", "TREE": "tree_accept_kernel"}
 
 
