@@ -503,10 +503,12 @@ def test_full_size_block_matrices(w12, name, n, k):
 
 
 @pytest.fixture(scope="module")
-def four_strip_mats(w12):
-    """At 5-32 rows on a 256-CU device the plan takes 4-strip tiles with the y
-    epilogue for Wgate|Wup 34816x5120 (long slices, x from the pre-pass) and
-    for Wq|Wk|Wv 8192x5120 (short slices, x read row-major, no pre-pass)."""
+def plan_mats(w12):
+    """At 5-32 rows on a 256-CU device the plan takes, with the y epilogue,
+    4-strip tiles and x from the pre-pass for Wgate|Wup 34816x5120 (21 units
+    per slice), 4-strip tiles and x read row-major for Wq|Wk|Wv 8192x5120 (5),
+    and 2-strip tiles with x from the pre-pass for 20480x5120 (12.5 units at
+    4 strips, 25 at 2)."""
     mats = {}
 
     def get(n, k):
@@ -518,14 +520,14 @@ def four_strip_mats(w12):
 
 
 @pytest.mark.parametrize("m", [5, 16, 32])
-@pytest.mark.parametrize("n,k", [(34816, 5120), (8192, 5120)])
-def test_full_size_four_strip_tiles(w12, four_strip_mats, n, k, m):
+@pytest.mark.parametrize("n,k", [(34816, 5120), (8192, 5120), (20480, 5120)])
+def test_full_size_plan_paths(w12, plan_mats, n, k, m):
     """Every channel of three 128-channel tiles (the first, one inside, the
     last) and 64 more against the oracle; repeats bit for bit on one
     workspace; bf16 output is the fp32 output rounded; the Q pass on two whole
     strips against the oracle's Q-pass weights."""
-    pw, w = four_strip_mats(n, k)
-    say("full four-strip", n, k, "m", m)
+    pw, w = plan_mats(n, k)
+    say("full plan paths", n, k, "m", m)
     x = synth.activations_bf16(m, k, 300 + m, device=DEV)
     ws = torch.zeros(w12.gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=DEV)
     y = w12.w12_gemm(pw, x, ws=ws).clone()
